@@ -1,0 +1,209 @@
+"""Benchmark of the convrot linear hot path on one MI355X.
+
+One step = the whole hot path on one batch: pack the activation (group-wise
+rotation + row absmax + int8 codes) once, then the three attention
+projections Q, K, V on that packed activation (int8 MFMA GEMM with the fused
+scale/bias epilogue).  Workload: X bf16 [4096, 3072] with LogNormal channel
+scales, three weights [3072, 3072], G = 256 (N total 9216).  Weight
+preparation is offline and not timed.  Inputs are resident in HBM before the
+timed region starts.
+
+Prints one JSON line: value = effective INT8 TOPS of the whole step
+(2*M*N*K / step time, the pack included), plus the pack's HBM GB/s, the
+roofline of the dominant kernel (the GEMM) from HIP events recorded on the
+launch stream around every launch in the timed region, and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0   # MI355X dense INT8 MFMA, 5.0 POP/s
+PEAK_HBM_GBPS = 8000.0    # MI355X HBM3E, 8 TB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qkv_4096x3072x9216")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, w, g, target_s):
+    """The oracle, as it stands, on a bounded sample of rows of the same workload."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import convrot_oracle as orc
+
+    cores = len(os.sched_getaffinity(0))
+    qws = [orc.quantize_weights(wt, g) for wt in inp["weights"]]  # offline, untimed
+
+    def run(rows):
+        x = inp["x64"][:rows]
+        t0 = time.perf_counter()
+        qx, sx = orc.pack_activations(x, g)
+        for (qw, sw), b in zip(qws, inp["biases"]):
+            orc.linear(qx, sx, qw, sw, b)
+        return time.perf_counter() - t0
+
+    with threadpool_limits(limits=cores):
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+        probe_rows = min(w.m, 128)
+        t_probe = run(probe_rows)
+        rows = int(min(w.m, max(probe_rows, probe_rows * target_s / max(t_probe, 1e-3))))
+        rows = max(16, (rows // 16) * 16)
+        t = run(rows)
+    n_total = sum(wt.shape[0] for wt in inp["weights"])
+    tops = 2.0 * rows * n_total * w.k / t / 1e12
+    return {
+        "value": tops, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+        "sample": f"{rows} of {w.m} rows, pack + {len(inp['weights'])} linears, "
+                  f"float64 NumPy oracle, {t:.2f} s wall",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import hadamard_rotated_int8_amd as cr
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cr.lib()  # fails loudly when the HIP library is missing
+    w = wl.WORKLOADS[args.workload]
+    g = 256
+    inp = wl.generate(w)
+    x = inp["x"].cuda()
+    qws = [cr.quantize_weights(torch.from_numpy(wt).cuda(), g, torch.from_numpy(b).cuda())
+           for wt, b in zip(inp["weights"], inp["biases"])]
+    m, k = w.m, w.k
+    packed = cr.PackedActivation(torch.empty((m, k), dtype=torch.int8, device="cuda"),
+                                 torch.empty((m,), dtype=torch.float32, device="cuda"), g)
+    ys = [torch.empty((m, q.q.shape[0]), dtype=torch.float32, device="cuda") for q in qws]
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        cr.pack_activations(x, g, out=packed)
+        if ev is not None:
+            ev[1].record()
+        for i, q in enumerate(qws):
+            cr.linear(packed, q, out=ys[i])
+            if ev is not None:
+                ev[2 + i].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    nev = 2 + len(qws)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        step(events[s])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+
+    pack_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    gemm_ms = np.array([[e[1 + i].elapsed_time(e[2 + i]) for i in range(len(qws))] for e in events])
+    n_total = sum(q.q.shape[0] for q in qws)
+    ops = 2.0 * m * n_total * k
+    value = ops / (ms_per_step * 1e-3) / 1e12
+    gemm_ops_per_launch = 2.0 * m * qws[0].q.shape[0] * k
+    gemm_avg_ms = float(gemm_ms.mean())
+    gemm_tops = gemm_ops_per_launch / (gemm_avg_ms * 1e-3) / 1e12
+    pack_bytes = m * k * (2 if x.dtype == torch.bfloat16 else 4) + m * k + 4 * m
+    pack_avg_ms = float(pack_ms.mean())
+    pack_gbps = pack_bytes / (pack_avg_ms * 1e-3) / 1e9
+
+    # Pack with the caches flushed (a 512 MB write between launches; not in the step).
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    cold = []
+    for _ in range(20):
+        flush.fill_(1.0)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        cr.pack_activations(x, g, out=packed)
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del flush
+    pack_cold_ms = float(np.median(cold))
+
+    out = {
+        "metric": "convrot linear effective INT8 TOPS at 4096x3072x9216; act-pack HBM GB/s",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "m": m, "k": k, "n": [q.q.shape[0] for q in qws], "group_size": g,
+            "x_dtype": w.x_dtype, "y_dtype": "f32",
+            "step": "1 pack + 3 linears on the packed activation",
+        },
+        "linear_tops": round(gemm_tops, 2),
+        "gemm_us_per_launch": round(gemm_avg_ms * 1e3, 3),
+        "pack_us": round(pack_avg_ms * 1e3, 3),
+        "pack_gbps": round(pack_gbps, 1),
+        "pack_us_cold": round(pack_cold_ms * 1e3, 3),
+        "pack_gbps_cold": round(pack_bytes / (pack_cold_ms * 1e-3) / 1e9, 1),
+        "pack_hbm_frac_cold": round(pack_bytes / (pack_cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "wall_s_timed": round(wall, 3),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "gemm_i8_kernel<256,192>",
+            "achieved": round(gemm_tops, 2),
+            "peak": PEAK_INT8_TOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, w, g, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,230 @@
+"""Python binding of libconvrot.so, the INT8 convrot linear layer for MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libconvrot.so.  The functions named ``convrot_*`` mirror the C ABI
+in include/convrot.h one to one (raw device pointers and sizes); the
+torch-level helpers below them only allocate outputs with torch and pass
+pointers plus torch's current HIP stream.
+
+torch is imported before the library is loaded so that the process holds a
+single HIP runtime (torch's), which the library then binds to.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch  # noqa: F401  (must precede loading the library; see above)
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libconvrot.so")
+
+# Status codes and enums (include/convrot.h).
+OK = 0
+ERR_NULL = 1
+ERR_SHAPE = 2
+ERR_GROUP = 3
+ERR_GROUP_MISMATCH = 4
+ERR_DTYPE = 5
+ERR_UNSUPPORTED = 6
+ERR_HIP = 7
+F32 = 0
+BF16 = 1
+I32 = 2
+ACT_NONE = 0
+ACT_GELU = 1
+MAX_K = 133136
+MAX_LOG4_GROUP = 7
+
+EXPORTED = (
+    "convrot_quantize_weights",
+    "convrot_pack_activations",
+    "convrot_linear",
+    "convrot_status_string",
+    "convrot_version",
+)
+
+
+class ConvrotError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class ConvrotPacked(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("scale", ctypes.c_void_p),
+        ("m", ctypes.c_int64),
+        ("k", ctypes.c_int64),
+        ("group_size", ctypes.c_int32),
+    ]
+
+
+class ConvrotWeights(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("scale", ctypes.c_void_p),
+        ("bias", ctypes.c_void_p),
+        ("n", ctypes.c_int64),
+        ("k", ctypes.c_int64),
+        ("group_size", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libconvrot.so (built in-tree); raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m hadamard_rotated_int8_amd.build`"
+            )
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        L.convrot_quantize_weights.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp]
+        L.convrot_quantize_weights.restype = ctypes.c_int
+        L.convrot_pack_activations.argtypes = [vp, i32, i64, i64, i64, i32,
+                                               ctypes.POINTER(ConvrotPacked), vp]
+        L.convrot_pack_activations.restype = ctypes.c_int
+        L.convrot_linear.argtypes = [ctypes.POINTER(ConvrotPacked), ctypes.POINTER(ConvrotWeights),
+                                     vp, i32, i64, i32, vp]
+        L.convrot_linear.restype = ctypes.c_int
+        L.convrot_status_string.argtypes = [ctypes.c_int]
+        L.convrot_status_string.restype = ctypes.c_char_p
+        L.convrot_version.argtypes = []
+        L.convrot_version.restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().convrot_status_string(int(status)).decode()
+
+
+# ---------------------------------------------------------------------------
+# Raw C ABI (device pointers as ints, stream as an int handle or None)
+# ---------------------------------------------------------------------------
+
+def convrot_quantize_weights(w, n, k, ldw, group_size, q_out, scale_out, stream=None) -> int:
+    return lib().convrot_quantize_weights(w, n, k, ldw, group_size, q_out, scale_out, stream)
+
+
+def convrot_pack_activations(x, x_dtype, m, k, ldx, group_size, out: ConvrotPacked,
+                             stream=None) -> int:
+    return lib().convrot_pack_activations(x, x_dtype, m, k, ldx, group_size, ctypes.byref(out),
+                                          stream)
+
+
+def convrot_linear(x: ConvrotPacked, w: ConvrotWeights, y, y_dtype, ldy, act=ACT_NONE,
+                   stream=None) -> int:
+    return lib().convrot_linear(ctypes.byref(x), ctypes.byref(w), y, y_dtype, ldy, act, stream)
+
+
+def convrot_version() -> int:
+    return int(lib().convrot_version())
+
+
+# ---------------------------------------------------------------------------
+# torch helpers: allocate outputs, pass pointers and the current stream
+# ---------------------------------------------------------------------------
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _require_cuda(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+@dataclass
+class PackedActivation:
+    """int8 rows and float32 row scales of one rotated activation."""
+
+    q: torch.Tensor       # int8 [m, k]
+    scale: torch.Tensor   # float32 [m]
+    group_size: int
+
+    def as_c(self) -> ConvrotPacked:
+        m, k = self.q.shape
+        return ConvrotPacked(_ptr(self.q), _ptr(self.scale), m, k, self.group_size)
+
+
+@dataclass
+class QuantizedWeights:
+    """int8 [n, k] codes, float32 [n] scales and optional float32 [n] bias."""
+
+    q: torch.Tensor
+    scale: torch.Tensor
+    bias: torch.Tensor | None
+    group_size: int
+
+    def as_c(self) -> ConvrotWeights:
+        n, k = self.q.shape
+        return ConvrotWeights(_ptr(self.q), _ptr(self.scale), _ptr(self.bias), n, k,
+                              self.group_size)
+
+
+def quantize_weights(w: torch.Tensor, group_size: int, bias: torch.Tensor | None = None
+                     ) -> QuantizedWeights:
+    """Offline W_rot = W R and per-row int8 codes (float32 W [n, k] on the device)."""
+    _require_cuda(w, "w")
+    if w.dtype != torch.float32 or w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be a float32 [n, k] device tensor with unit column stride")
+    n, k = w.shape
+    q = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    s = torch.empty((n,), dtype=torch.float32, device=w.device)
+    st = convrot_quantize_weights(_ptr(w), n, k, w.stride(0), group_size, _ptr(q), _ptr(s),
+                                  _stream())
+    if st != OK:
+        raise ConvrotError(st, "convrot_quantize_weights")
+    return QuantizedWeights(q, s, bias, group_size)
+
+
+def pack_activations(x: torch.Tensor, group_size: int, out: PackedActivation | None = None
+                     ) -> PackedActivation:
+    """Rotate and quantise the rows of x (bf16 or float32 [m, k] on the device)."""
+    _require_cuda(x, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [m, k] with unit column stride")
+    dt = {torch.float32: F32, torch.bfloat16: BF16}.get(x.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported activation dtype {x.dtype}")
+    m, k = x.shape
+    if out is None:
+        out = PackedActivation(torch.empty((m, k), dtype=torch.int8, device=x.device),
+                               torch.empty((m,), dtype=torch.float32, device=x.device),
+                               group_size)
+    c = ConvrotPacked(_ptr(out.q), _ptr(out.scale), 0, 0, 0)
+    st = convrot_pack_activations(_ptr(x), dt, m, k, x.stride(0), group_size, c, _stream())
+    if st != OK:
+        raise ConvrotError(st, "convrot_pack_activations")
+    out.group_size = group_size
+    return out
+
+
+def linear(x: PackedActivation, w: QuantizedWeights, out: torch.Tensor | None = None,
+           raw_i32: bool = False, gelu: bool = False) -> torch.Tensor:
+    """Y = (Q_x Q_w^T) s_x s_w + b (float32 [m, n]); raw_i32 returns the int32 A."""
+    m = x.q.shape[0]
+    n = w.q.shape[0]
+    dtype = torch.int32 if raw_i32 else torch.float32
+    if out is None:
+        out = torch.empty((m, n), dtype=dtype, device=x.q.device)
+    if out.dtype != dtype or out.dim() != 2 or out.stride(1) != 1:
+        raise ValueError("out has the wrong dtype or layout")
+    st = convrot_linear(x.as_c(), w.as_c(), _ptr(out), I32 if raw_i32 else F32, out.stride(0),
+                        ACT_GELU if gelu else ACT_NONE, _stream())
+    if st != OK:
+        raise ConvrotError(st, "convrot_linear")
+    return out

@@ -1,0 +1,123 @@
+// C ABI of libconvrot.so: argument validation and dispatch to the HIP kernels.
+//
+// Every check runs on the host before any HIP call, so an invalid call
+// returns a status code and touches neither the GPU nor the HIP runtime.
+#include <hip/hip_runtime.h>
+
+#include "../../include/convrot.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// log4 of a valid group size (1, 4, ..., 4^7), or -1.
+int log4_of(int32_t g) {
+  for (int n = 0; n <= CONVROT_MAX_LOG4_GROUP; ++n)
+    if (g == (int32_t(1) << (2 * n))) return n;
+  return -1;
+}
+
+convrot_status check_k_group(int64_t k, int32_t group_size, int* log4g) {
+  if (k < 1 || k > CONVROT_MAX_K) return CONVROT_ERR_SHAPE;
+  const int n = log4_of(group_size);
+  if (n < 0 || k % group_size != 0) return CONVROT_ERR_GROUP;
+  if (k % 16 != 0) return CONVROT_ERR_UNSUPPORTED;
+  *log4g = n;
+  return CONVROT_OK;
+}
+
+convrot_status from_hip(hipError_t e) { return e == hipSuccess ? CONVROT_OK : CONVROT_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* convrot_status_string(convrot_status s) {
+  switch (s) {
+    case CONVROT_OK: return "ok";
+    case CONVROT_ERR_NULL: return "a required pointer is NULL";
+    case CONVROT_ERR_SHAPE: return "m, n or k out of range, or ld smaller than the row";
+    case CONVROT_ERR_GROUP: return "group size is not a power of four in 1..16384 dividing k";
+    case CONVROT_ERR_GROUP_MISMATCH: return "packed activation and weights differ in k or group size";
+    case CONVROT_ERR_DTYPE: return "unsupported dtype or activation";
+    case CONVROT_ERR_UNSUPPORTED: return "k % 16 != 0, or a pointer or stride is not 16-byte aligned";
+    case CONVROT_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t convrot_version(void) { return 100; }
+
+convrot_status convrot_quantize_weights(const float* w, int64_t n, int64_t k, int64_t ldw,
+                                        int32_t group_size, int8_t* q_out, float* scale_out,
+                                        void* stream) {
+  int log4g = 0;
+  const convrot_status st = check_k_group(k, group_size, &log4g);
+  if (st != CONVROT_OK) return st;
+  if (n < 0 || n > kMaxRows || ldw < k) return CONVROT_ERR_SHAPE;
+  if (n == 0) return CONVROT_OK;
+  if (!w || !q_out || !scale_out) return CONVROT_ERR_NULL;
+  if (!aligned16(q_out)) return CONVROT_ERR_UNSUPPORTED;
+  return from_hip(convrot::launch_wprep(w, n, k, ldw, log4g, q_out, scale_out,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+convrot_status convrot_pack_activations(const void* x, int32_t x_dtype, int64_t m, int64_t k,
+                                        int64_t ldx, int32_t group_size, convrot_packed* out,
+                                        void* stream) {
+  if (!out) return CONVROT_ERR_NULL;
+  int log4g = 0;
+  const convrot_status st = check_k_group(k, group_size, &log4g);
+  if (st != CONVROT_OK) return st;
+  if (m < 0 || m > kMaxRows || ldx < k) return CONVROT_ERR_SHAPE;
+  if (x_dtype != CONVROT_F32 && x_dtype != CONVROT_BF16) return CONVROT_ERR_DTYPE;
+  if (m > 0 && (!x || !out->q || !out->scale)) return CONVROT_ERR_NULL;
+  const int64_t esize = (x_dtype == CONVROT_F32) ? 4 : 2;
+  if (m > 0 && (!aligned16(x) || !aligned16(out->q) || (ldx * esize) % 16 != 0))
+    return CONVROT_ERR_UNSUPPORTED;
+  out->m = m;
+  out->k = k;
+  out->group_size = group_size;
+  if (m == 0) return CONVROT_OK;
+  return from_hip(convrot::launch_pack(x, x_dtype == CONVROT_BF16, ldx, m, k, log4g, out->q,
+                                       out->scale, static_cast<hipStream_t>(stream)));
+}
+
+convrot_status convrot_linear(const convrot_packed* x, const convrot_weights* w, void* y,
+                              int32_t y_dtype, int64_t ldy, int32_t act, void* stream) {
+  if (!x || !w) return CONVROT_ERR_NULL;
+  int log4g = 0;
+  convrot_status st = check_k_group(x->k, x->group_size, &log4g);
+  if (st != CONVROT_OK) return st;
+  if (w->k != x->k || w->group_size != x->group_size) return CONVROT_ERR_GROUP_MISMATCH;
+  if (x->m < 0 || x->m > kMaxRows || w->n < 0 || w->n > kMaxRows) return CONVROT_ERR_SHAPE;
+  if (y_dtype != CONVROT_F32 && y_dtype != CONVROT_I32) return CONVROT_ERR_DTYPE;
+  if (act != CONVROT_ACT_NONE && act != CONVROT_ACT_GELU) return CONVROT_ERR_DTYPE;
+  if (y_dtype == CONVROT_I32 && act != CONVROT_ACT_NONE) return CONVROT_ERR_DTYPE;
+  if (ldy < w->n) return CONVROT_ERR_SHAPE;
+  if (x->m == 0 || w->n == 0) return CONVROT_OK;
+  if (!x->q || !w->q || !y) return CONVROT_ERR_NULL;
+  if (y_dtype == CONVROT_F32 && (!x->scale || !w->scale)) return CONVROT_ERR_NULL;
+  // y needs only its element alignment; 16-byte rows take the vector-store path.
+  if (!aligned16(x->q) || !aligned16(w->q) || (reinterpret_cast<uintptr_t>(y) & 3u) != 0)
+    return CONVROT_ERR_UNSUPPORTED;
+  convrot::GemmArgs a;
+  a.qx = x->q;
+  a.sx = x->scale;
+  a.qw = w->q;
+  a.sw = w->scale;
+  a.bias = w->bias;
+  a.y = y;
+  a.m = x->m;
+  a.n = w->n;
+  a.k = x->k;
+  a.ldy = ldy;
+  a.raw_i32 = (y_dtype == CONVROT_I32);
+  a.gelu = (act == CONVROT_ACT_GELU);
+  return from_hip(convrot::launch_gemm(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// Host-side launchers of the convrot kernels (internal to libconvrot.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace convrot {
+
+// Launch shape of the activation pack for a row length k (k % 16 == 0).
+struct PackPlan {
+  int threads;            // workgroup size, 64..1024
+  int chunks_per_thread;  // 16-feature chunks per thread per segment (1, 2 or 4)
+  int segments;           // > 1 only for very long rows: X is then read twice
+};
+PackPlan plan_pack(int64_t k);
+
+hipError_t launch_pack(const void* x, bool bf16, int64_t ldx, int64_t m, int64_t k, int log4g,
+                       int8_t* q, float* scale, hipStream_t stream);
+
+hipError_t launch_wprep(const float* w, int64_t n, int64_t k, int64_t ldw, int log4g,
+                        int8_t* q, float* scale, hipStream_t stream);
+
+struct GemmArgs {
+  const int8_t* qx;   // [m, k]
+  const float* sx;    // [m]
+  const int8_t* qw;   // [n, k]
+  const float* sw;    // [n]
+  const float* bias;  // [n] or nullptr
+  void* y;            // [m, ldy] float32 or int32
+  int64_t m, n, k, ldy;
+  bool raw_i32;
+  bool gelu;
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+
+}  // namespace convrot

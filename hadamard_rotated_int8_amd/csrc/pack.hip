@@ -1,0 +1,328 @@
+// Activation pack: group-wise Hadamard rotation + row absmax + int8 codes.
+//
+// Implements the runtime half of the stable-diffusion.cpp page "INT8 Convrot
+// Safetensors", section "Runtime activation quantization": every row of X is
+// rotated by the block-diagonal R (R_G = normalised Kronecker power of H4 on
+// each contiguous group of G = 4^n features, section "How INT8 convrot works"),
+// then one scale per row s = max|X_rot| / 127 and codes
+// Q = clamp(round(X_rot / s), -127, 127), packed as int8 rows + float32 scales.
+//
+// Design (gfx950, one pass over HBM, HBM-bound):
+//   * one workgroup per row (rows strided over the grid); T = 64..1024 threads;
+//   * a thread owns "chunks" of 16 consecutive features, loaded with 16-byte
+//     vector loads (bf16: 2 loads, fp32: 4 loads);
+//   * the base-4 digits of the in-group index are transformed in any order
+//     (every factor of the Kronecker power is the same H4):
+//       digits 0,1 (feature bits 0-3)  : inside the thread's registers,
+//       digit 2    (lane bits 0-1)     : DPP quad permutations,
+//       digit 3    (lane bits 2-3)     : DPP row rotations (see chunk_of_thread),
+//       digit 4    (lane bits 4-5)     : cross-row lane shuffles,
+//       digits 5,6 (wave bits)         : through LDS;
+//   * the butterfly is unnormalised, y_d = sum(x) - 2 x_{3-d} = 2 (H4 x)_d; the
+//     factor 2^n is exact and is taken out of the scale, so every rounding is
+//     that of the normalised butterfly;
+//   * the row absmax is reduced across lanes and then across waves in LDS;
+//   * the code decision is made in float32: s = m/127 (IEEE division), then
+//     v = RN(x/s) via a correctly rounded reciprocal plus one FMA correction,
+//     then round-half-away; the int8 codes leave as 16-byte stores.
+#include "common.h"
+#include "kernels.h"
+
+namespace convrot {
+namespace {
+
+// Radix-4 butterfly on four registers: returns 2 * H4 * x (unnormalised).
+CR_DEVICE void h4_reg(float& a, float& b, float& c, float& d) {
+  const float s = (a + b) + (c + d);
+  const float y0 = __builtin_fmaf(-2.f, d, s);
+  const float y1 = __builtin_fmaf(-2.f, c, s);
+  const float y2 = __builtin_fmaf(-2.f, b, s);
+  const float y3 = __builtin_fmaf(-2.f, a, s);
+  a = y0;
+  b = y1;
+  c = y2;
+  d = y3;
+}
+
+// Digit held by lane bits 0-1 (natural order): partner 3-d is lane ^ 3.
+CR_DEVICE float h4_quad(float x) {
+  const float t = x + dpp_f32<kDppQuadSwap1>(x);
+  const float s = t + dpp_f32<kDppQuadSwap2>(t);
+  return __builtin_fmaf(-2.f, dpp_f32<kDppQuadRev>(x), s);
+}
+
+// Digit held by lane bits 2-3.  The lane -> digit map is d = 2*b3 + (b2 ^ b3),
+// so the lane holding digit 3-d is lane ^ 8, one row rotation by 8.
+CR_DEVICE float h4_row(float x) {
+  const float t = x + dpp_f32<kDppRowRor4>(x);
+  const float s = t + dpp_f32<kDppRowRor8>(t);
+  return __builtin_fmaf(-2.f, dpp_f32<kDppRowRor8>(x), s);
+}
+
+// Digit held by lane bits 4-5 (natural order): partner is lane ^ 48.
+CR_DEVICE float h4_wave(float x) {
+  const float a = __shfl_xor(x, 16);
+  const float b = __shfl_xor(x, 32);
+  const float c = __shfl_xor(x, 48);
+  const float s = (x + a) + (b + c);
+  return __builtin_fmaf(-2.f, c, s);
+}
+
+// Thread t owns chunk (t with bit 2 replaced by bit2 ^ bit3) of each block of
+// T chunks, which realises the lane -> digit map used by h4_row.  It permutes
+// chunks only inside aligned groups of 16 lanes, so loads stay coalesced.
+CR_DEVICE int chunk_of_thread(int t) { return t ^ ((t >> 1) & 4); }
+
+CR_DEVICE void load16(const float* __restrict__ p, float* v) {
+  const f32x4* p4 = reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 f = __builtin_nontemporal_load(p4 + i);
+    v[4 * i + 0] = f.x;
+    v[4 * i + 1] = f.y;
+    v[4 * i + 2] = f.z;
+    v[4 * i + 3] = f.w;
+  }
+}
+
+CR_DEVICE void load16(const uint16_t* __restrict__ p, float* v) {
+  const u32x4* p4 = reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const u32x4 u = __builtin_nontemporal_load(p4 + i);
+    v[8 * i + 0] = bf16_lo(u.x);
+    v[8 * i + 1] = bf16_hi(u.x);
+    v[8 * i + 2] = bf16_lo(u.y);
+    v[8 * i + 3] = bf16_hi(u.y);
+    v[8 * i + 4] = bf16_lo(u.z);
+    v[8 * i + 5] = bf16_hi(u.z);
+    v[8 * i + 6] = bf16_lo(u.w);
+    v[8 * i + 7] = bf16_hi(u.w);
+  }
+}
+
+CR_DEVICE uint32_t pack4(int a, int b, int c, int d) {
+  return (uint32_t(a) & 0xFFu) | ((uint32_t(b) & 0xFFu) << 8) | ((uint32_t(c) & 0xFFu) << 16) |
+         (uint32_t(d) << 24);
+}
+
+// Rotate the 16 values of one chunk along the digits that live in registers
+// and in lanes of the same wave.
+CR_DEVICE void rotate_in_wave(float* v, int log4g) {
+  if (log4g >= 1) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) h4_reg(v[4 * a], v[4 * a + 1], v[4 * a + 2], v[4 * a + 3]);
+  }
+  if (log4g >= 2) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) h4_reg(v[a], v[a + 4], v[a + 8], v[a + 12]);
+  }
+  if (log4g >= 3) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = h4_quad(v[e]);
+  }
+  if (log4g >= 4) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = h4_row(v[e]);
+  }
+  if (log4g >= 5) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = h4_wave(v[e]);
+  }
+}
+
+// Digits 5 and 6 live in wave-index bits 0-1 and 2-3; exchange through LDS.
+// Every thread of the block must call this (it contains barriers).
+CR_DEVICE void rotate_across_waves(float* v, int log4g, float4* buf, int t) {
+  for (int dg = 5; dg < log4g; ++dg) {
+    const int sh = 6 + 2 * (dg - 5);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      buf[t * 4 + i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+    __syncthreads();
+    const int dd = (t >> sh) & 3;
+    const int base = t & ~(3 << sh);
+    float sum[16], rev[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sum[e] = v[e];
+#pragma unroll
+    for (int d2 = 0; d2 < 4; ++d2) {
+      if (d2 == dd) continue;
+      const int tt = base | (d2 << sh);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 f = buf[tt * 4 + i];
+        sum[4 * i + 0] += f.x;
+        sum[4 * i + 1] += f.y;
+        sum[4 * i + 2] += f.z;
+        sum[4 * i + 3] += f.w;
+        if (d2 == 3 - dd) {
+          rev[4 * i + 0] = f.x;
+          rev[4 * i + 1] = f.y;
+          rev[4 * i + 2] = f.z;
+          rev[4 * i + 3] = f.w;
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = __builtin_fmaf(-2.f, rev[e], sum[e]);
+  }
+}
+
+template <typename InT, int CPT>
+CR_DEVICE void load_rotate_segment(const InT* __restrict__ xr, int seg, int nch, int log4g,
+                                   float (&v)[CPT][16], float4* buf, int t, int T) {
+  const int tp = chunk_of_thread(t);
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int j = (seg * CPT + c) * T + tp;
+    if (j < nch) {
+      load16(xr + (int64_t)j * 16, v[c]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[c][e] = 0.f;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) rotate_in_wave(v[c], log4g);
+  if (log4g >= 6) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) rotate_across_waves(v[c], log4g, buf, t);
+  }
+}
+
+template <int CPT>
+CR_DEVICE float local_absmax(const float (&v)[CPT][16]) {
+  float m = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[c][e]));
+  return m;
+}
+
+template <int CPT>
+CR_DEVICE void quantize_store(const float (&v)[CPT][16], int seg, int nch, float s_un, float r,
+                              int8_t* __restrict__ qr, int t, int T) {
+  const int tp = chunk_of_thread(t);
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int j = (seg * CPT + c) * T + tp;
+    if (j >= nch) continue;
+    int qi[16];
+    if (s_un != 0.f) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        qi[e] = clamp127(round_half_away_small(div_by_recip(v[c][e], s_un, r)));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) qi[e] = 0;
+    }
+    uint4 o;
+    o.x = pack4(qi[0], qi[1], qi[2], qi[3]);
+    o.y = pack4(qi[4], qi[5], qi[6], qi[7]);
+    o.z = pack4(qi[8], qi[9], qi[10], qi[11]);
+    o.w = pack4(qi[12], qi[13], qi[14], qi[15]);
+    *reinterpret_cast<uint4*>(qr + (int64_t)j * 16) = o;
+  }
+}
+
+template <typename InT, int CPT>
+__global__ __launch_bounds__(1024) void pack_kernel(const InT* __restrict__ x, int64_t ldx,
+                                                    int m, int k, int log4g, int nseg,
+                                                    int8_t* __restrict__ q,
+                                                    float* __restrict__ scale) {
+  extern __shared__ float4 lds_buf[];  // T * 16 floats, only when log4g >= 6
+  __shared__ float wave_max[16];
+  const int T = blockDim.x;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int nwaves = T >> 6;
+  const int nch = k >> 4;
+
+  for (int row = blockIdx.x; row < m; row += gridDim.x) {
+    const InT* xr = x + (int64_t)row * ldx;
+    int8_t* qr = q + (int64_t)row * k;
+    float v[CPT][16];
+    float mx = 0.f;
+    for (int seg = 0; seg < nseg; ++seg) {
+      load_rotate_segment<InT, CPT>(xr, seg, nch, log4g, v, lds_buf, t, T);
+      mx = fmaxf(mx, local_absmax<CPT>(v));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    if (lane == 0) wave_max[wave] = mx;
+    __syncthreads();
+    mx = wave_max[0];
+    for (int w = 1; w < nwaves; ++w) mx = fmaxf(mx, wave_max[w]);
+    __syncthreads();  // wave_max is rewritten for the next row
+
+    // Undo the unnormalised butterfly's exact factor 2^n, then s = max / 127.
+    const float s = ldexpf(mx, -log4g) / 127.0f;
+    if (t == 0) scale[row] = s;
+    const float s_un = ldexpf(s, log4g);  // x_un / s_un == x / s exactly
+    const float r = (s_un != 0.f) ? 1.0f / s_un : 0.f;
+    if (nseg == 1) {
+      quantize_store<CPT>(v, 0, nch, s_un, r, qr, t, T);
+    } else {
+      for (int seg = 0; seg < nseg; ++seg) {
+        load_rotate_segment<InT, CPT>(xr, seg, nch, log4g, v, lds_buf, t, T);
+        quantize_store<CPT>(v, seg, nch, s_un, r, qr, t, T);
+      }
+    }
+  }
+}
+
+template <typename InT, int CPT>
+hipError_t launch_pack_t(const void* x, int64_t ldx, int m, int k, int log4g, int threads,
+                         int nseg, int8_t* q, float* scale, hipStream_t stream) {
+  const int grid = m < (1 << 20) ? m : (1 << 20);
+  const size_t lds = (log4g >= 6) ? size_t(threads) * 16 * sizeof(float) : 0;
+  hipLaunchKernelGGL((pack_kernel<InT, CPT>), dim3(grid), dim3(threads), lds, stream,
+                     static_cast<const InT*>(x), ldx, m, k, log4g, nseg, q, scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+PackPlan plan_pack(int64_t k) {
+  PackPlan p;
+  const int64_t nch = k / 16;
+  int64_t waves = (nch + 63) / 64;
+  if (waves > 16) waves = 16;
+  p.threads = int(waves * 64);
+  const int64_t per_thread = (nch + p.threads - 1) / p.threads;
+  if (per_thread <= 1) {
+    p.chunks_per_thread = 1;
+    p.segments = 1;
+  } else if (per_thread <= 2) {
+    p.chunks_per_thread = 2;
+    p.segments = 1;
+  } else if (per_thread <= 4) {
+    p.chunks_per_thread = 4;
+    p.segments = 1;
+  } else {
+    p.chunks_per_thread = 4;
+    p.segments = int((per_thread + 3) / 4);
+  }
+  return p;
+}
+
+hipError_t launch_pack(const void* x, bool bf16, int64_t ldx, int64_t m, int64_t k, int log4g,
+                       int8_t* q, float* scale, hipStream_t stream) {
+  const PackPlan p = plan_pack(k);
+  const int mi = int(m), ki = int(k);
+  switch (p.chunks_per_thread * 2 + (bf16 ? 1 : 0)) {
+    case 2: return launch_pack_t<float, 1>(x, ldx, mi, ki, log4g, p.threads, p.segments, q, scale, stream);
+    case 3: return launch_pack_t<uint16_t, 1>(x, ldx, mi, ki, log4g, p.threads, p.segments, q, scale, stream);
+    case 4: return launch_pack_t<float, 2>(x, ldx, mi, ki, log4g, p.threads, p.segments, q, scale, stream);
+    case 5: return launch_pack_t<uint16_t, 2>(x, ldx, mi, ki, log4g, p.threads, p.segments, q, scale, stream);
+    case 8: return launch_pack_t<float, 4>(x, ldx, mi, ki, log4g, p.threads, p.segments, q, scale, stream);
+    case 9: return launch_pack_t<uint16_t, 4>(x, ldx, mi, ki, log4g, p.threads, p.segments, q, scale, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace convrot

@@ -40,6 +40,7 @@ All arrays are NumPy; floats are float64 unless a step states float32.
 
 from __future__ import annotations
 
+import functools
 import math
 
 import numpy as np
@@ -79,8 +80,9 @@ def log4_group(group_size: int) -> int:
     return n
 
 
+@functools.lru_cache(maxsize=4)
 def rotation_matrix(group_size: int) -> np.ndarray:
-    """R_G, the normalised Kronecker power of H4 with G = 4**n rows.
+    """R_G, the normalised Kronecker power of H4 with G = 4**n rows (read-only, cached).
 
     [ICS, How INT8 convrot works]: for G = 4^n the transform is the Kronecker
     power of H4; H4 already carries the 1/2, so the power is orthonormal and no
@@ -90,6 +92,7 @@ def rotation_matrix(group_size: int) -> np.ndarray:
     r = np.ones((1, 1), dtype=np.float64)
     for _ in range(n):
         r = np.kron(r, h4())
+    r.flags.writeable = False
     return r
 
 

@@ -1,0 +1,163 @@
+"""C-ABI boundary tests that need no GPU.
+
+libconvrot.so validates every argument on the host before any HIP call, so
+each invalid call below returns its status code without touching a device.
+Every call here fails validation; none of them launches a kernel.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import hadamard_rotated_int8_amd as cr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "convrot.h")
+
+FAKE = 0x10000  # a 16-byte aligned non-null address; only used where validation fails first
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(convrot_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert set(names) == set(cr.EXPORTED)
+    L = cr.lib()
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    assert int(re.search(r"#define CONVROT_MAX_K (\d+)", text).group(1)) == cr.MAX_K
+    assert cr.MAX_K % 16 == 0 and cr.MAX_K * 127 * 127 < 2**31
+    assert (cr.MAX_K + 16) * 127 * 127 >= 2**31
+    for name, val in [("CONVROT_OK", 0), ("CONVROT_ERR_NULL", 1), ("CONVROT_ERR_SHAPE", 2),
+                      ("CONVROT_ERR_GROUP", 3), ("CONVROT_ERR_GROUP_MISMATCH", 4),
+                      ("CONVROT_ERR_DTYPE", 5), ("CONVROT_ERR_UNSUPPORTED", 6),
+                      ("CONVROT_ERR_HIP", 7)]:
+        assert re.search(rf"{name} = {val}\b", text), name
+
+
+def test_version_and_status_strings():
+    assert cr.convrot_version() == 100
+    for s in range(8):
+        assert cr.status_string(s)
+    assert cr.status_string(99) == "unknown status"
+
+
+def _pack(x=FAKE, dt=cr.BF16, m=4, k=1024, ldx=None, g=256, q=FAKE, s=FAKE, out=True):
+    p = cr.ConvrotPacked(q, s, 0, 0, 0)
+    if not out:
+        return cr.lib().convrot_pack_activations(x, dt, m, k, k if ldx is None else ldx, g,
+                                                 None, None)
+    return cr.convrot_pack_activations(x, dt, m, k, k if ldx is None else ldx, g, p), p
+
+
+@pytest.mark.parametrize("g", [0, -4, 2, 3, 8, 32, 128, 255, 512, 4**8, 2**31 - 1])
+def test_pack_rejects_bad_group(g):
+    st, _ = _pack(g=g, k=4**8 * 2)
+    assert st == cr.ERR_GROUP
+
+
+def test_pack_rejects_group_not_dividing_k():
+    st, _ = _pack(g=256, k=1024 + 64)
+    assert st == cr.ERR_GROUP
+    st, _ = _pack(g=16384, k=8192)  # G > K
+    assert st == cr.ERR_GROUP
+
+
+def test_pack_shape_errors():
+    assert _pack(k=0, g=1)[0] == cr.ERR_SHAPE
+    assert _pack(k=cr.MAX_K + 16, g=16)[0] == cr.ERR_SHAPE
+    assert _pack(m=-1)[0] == cr.ERR_SHAPE
+    assert _pack(m=2**31)[0] == cr.ERR_SHAPE
+    assert _pack(ldx=1000)[0] == cr.ERR_SHAPE
+
+
+def test_pack_unsupported_and_dtype():
+    assert _pack(k=20, g=4)[0] == cr.ERR_UNSUPPORTED          # k % 16 != 0 (a valid G)
+    assert _pack(x=FAKE + 8)[0] == cr.ERR_UNSUPPORTED          # misaligned input
+    assert _pack(q=FAKE + 4)[0] == cr.ERR_UNSUPPORTED          # misaligned codes
+    assert _pack(ldx=1028, dt=cr.BF16)[0] == cr.ERR_UNSUPPORTED  # row stride not 16 bytes
+    assert _pack(dt=cr.I32)[0] == cr.ERR_DTYPE
+    assert _pack(dt=7)[0] == cr.ERR_DTYPE
+
+
+def test_pack_null_pointers():
+    assert _pack(out=False) == cr.ERR_NULL
+    assert _pack(x=None)[0] == cr.ERR_NULL
+    assert _pack(q=None)[0] == cr.ERR_NULL
+    assert _pack(s=None)[0] == cr.ERR_NULL
+
+
+def test_pack_empty_is_a_no_op():
+    st, p = _pack(x=None, q=None, s=None, m=0, k=3072, g=256)
+    assert st == cr.OK
+    assert (p.m, p.k, p.group_size) == (0, 3072, 256)
+
+
+def _lin(m=16, k=1024, gx=256, n=512, kw=None, gw=None, y=FAKE, ydt=cr.F32, ldy=None,
+         act=cr.ACT_NONE, qx=FAKE, sx=FAKE, qw=FAKE, sw=FAKE, bias=None):
+    px = cr.ConvrotPacked(qx, sx, m, k, gx)
+    w = cr.ConvrotWeights(qw, sw, bias, n, k if kw is None else kw, gx if gw is None else gw)
+    return cr.convrot_linear(px, w, y, ydt, n if ldy is None else ldy, act)
+
+
+def test_linear_group_mismatch():
+    assert _lin(gw=64) == cr.ERR_GROUP_MISMATCH
+    assert _lin(kw=2048) == cr.ERR_GROUP_MISMATCH
+
+
+def test_linear_validation():
+    assert cr.lib().convrot_linear(None, None, None, 0, 0, 0, None) == cr.ERR_NULL
+    assert _lin(gx=255) == cr.ERR_GROUP
+    assert _lin(m=-1) == cr.ERR_SHAPE
+    assert _lin(n=-5) == cr.ERR_SHAPE
+    assert _lin(ldy=100) == cr.ERR_SHAPE
+    assert _lin(ydt=cr.BF16) == cr.ERR_DTYPE
+    assert _lin(act=5) == cr.ERR_DTYPE
+    assert _lin(ydt=cr.I32, act=cr.ACT_GELU) == cr.ERR_DTYPE
+    assert _lin(y=None) == cr.ERR_NULL
+    assert _lin(qx=None) == cr.ERR_NULL
+    assert _lin(sw=None) == cr.ERR_NULL
+    assert _lin(y=FAKE + 2) == cr.ERR_UNSUPPORTED  # y needs 4-byte alignment only
+    assert _lin(qw=FAKE + 1) == cr.ERR_UNSUPPORTED
+    assert _lin(qx=FAKE + 8) == cr.ERR_UNSUPPORTED
+    assert _lin(k=1040, gx=16, kw=1040, gw=16, qx=None) == cr.ERR_NULL  # ragged K is accepted
+
+
+def test_linear_empty_is_a_no_op():
+    assert _lin(m=0, y=None, qx=None) == cr.OK
+    assert _lin(n=0, y=None, qw=None, ldy=0) == cr.OK
+
+
+def _qw(w=FAKE, n=512, k=1024, ldw=None, g=256, q=FAKE, s=FAKE):
+    return cr.convrot_quantize_weights(w, n, k, k if ldw is None else ldw, g, q, s)
+
+
+def test_quantize_weights_validation():
+    assert _qw(g=8) == cr.ERR_GROUP
+    assert _qw(k=1024 + 64) == cr.ERR_GROUP
+    assert _qw(k=0, g=1) == cr.ERR_SHAPE
+    assert _qw(n=-1) == cr.ERR_SHAPE
+    assert _qw(ldw=512) == cr.ERR_SHAPE
+    assert _qw(w=None) == cr.ERR_NULL
+    assert _qw(q=None) == cr.ERR_NULL
+    assert _qw(s=None) == cr.ERR_NULL
+    assert _qw(q=FAKE + 2) == cr.ERR_UNSUPPORTED
+    assert _qw(n=0, w=None, q=None, s=None) == cr.OK
+
+
+def test_struct_layouts_match_c():
+    # int8_t* q; float* scale; int64 m; int64 k; int32 group_size  -> 36 bytes + padding
+    assert ctypes.sizeof(cr.ConvrotPacked) == 40
+    assert cr.ConvrotPacked.m.offset == 16 and cr.ConvrotPacked.group_size.offset == 32
+    assert ctypes.sizeof(cr.ConvrotWeights) == 48
+    assert cr.ConvrotWeights.n.offset == 24 and cr.ConvrotWeights.group_size.offset == 40

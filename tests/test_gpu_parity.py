@@ -1,0 +1,428 @@
+"""GPU parity: the HIP path against the CPU oracle, through the C ABI.
+
+Tolerances (stated by the workload definition and derived in the design doc):
+  * Q_w and s_w bit-exact (both sides decide in float64);
+  * Q_x within +-1 on at most 0.1% of elements, s_x within 1e-6 relative
+    (the device rotates in float32 with a butterfly, the oracle rotates in
+    float64 and rounds once; the decision itself is float32 on both sides);
+  * A (raw int32) bit-exact when both sides get the same Q_x and Q_w;
+  * Y within 1e-3 * s_x * s_w * K * 127 per element and a mean relative
+    (aggregate L1) error of at most 1e-4 against the oracle's dequantised Y.
+Inputs come from workloads.py (seeded, shared by both sides); expected values
+come only from oracle/.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import hadamard_rotated_int8_amd as cr
+import workloads as wl
+from oracle import convrot_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+Q_MISMATCH_FRAC = 1e-3
+S_REL = 1e-6
+Y_ELEM = 1e-3
+Y_MEAN_REL = 1e-4
+GELU_LIPSCHITZ = 1.13  # max |d/dx x*Phi(x)| = 1.1289...
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    cr.lib()
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def _say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a)) if isinstance(a, np.ndarray) else a
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def check_pack(q_dev, s_dev, q_or, s_or, what=""):
+    q_dev = np.asarray(q_dev).astype(np.int32)
+    q_or = np.asarray(q_or).astype(np.int32)
+    assert q_dev.shape == q_or.shape
+    zero = s_or == 0
+    assert np.all(s_dev[zero] == 0), f"{what}: zero rows must have scale 0"
+    nz = ~zero
+    if np.any(nz):
+        rel = np.abs(s_dev[nz].astype(np.float64) - s_or[nz]) / s_or[nz]
+        assert rel.max() <= S_REL, f"{what}: s_x rel err {rel.max():.3g}"
+    d = q_dev - q_or
+    assert np.abs(d).max(initial=0) <= 1, f"{what}: code differs by {np.abs(d).max()}"
+    frac = np.count_nonzero(d) / max(1, d.size)
+    assert frac <= Q_MISMATCH_FRAC, f"{what}: {frac:.3%} codes differ"
+    assert q_dev.min(initial=0) >= -127 and q_dev.max(initial=0) <= 127
+    return frac
+
+
+def check_y(y_dev, y_or, sx, sw, k, gelu=False, what=""):
+    y_dev = np.asarray(y_dev, dtype=np.float64)
+    bound = Y_ELEM * sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :] * k * 127
+    if gelu:
+        bound = bound * GELU_LIPSCHITZ
+    err = np.abs(y_dev - y_or)
+    worst = np.max(err - bound)
+    assert worst <= 0, f"{what}: per-element bound exceeded by {worst:.3g}"
+    rel = err.sum() / np.abs(y_or).sum()
+    assert rel <= Y_MEAN_REL, f"{what}: mean relative error {rel:.3g}"
+    return rel
+
+
+# ---------------------------------------------------------------------------
+# Pack
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("g", [1, 4, 16, 64, 256, 1024, 4096, 16384])
+def test_pack_crafted_rows_exact(g):
+    """X = y R with half-integer y: the device butterfly is exact, so codes are exact."""
+    k = max(g, 2048)
+    y = wl.crafted_rotated_rows(g, k, 8, seed=g)
+    x = orc.rotate(y, g)  # exactly representable in float32
+    assert np.array_equal(x.astype(np.float32).astype(np.float64), x)
+    _say(f"pack crafted G={g} K={k}")
+    p = cr.pack_activations(dev(x.astype(np.float32)), g)
+    q, s = host(p.q), host(p.scale)
+    q_or, s_or = orc.pack_activations(x, g)
+    assert np.all(s == 1.0)
+    assert np.array_equal(q, q_or)
+
+
+@pytest.mark.parametrize("g", [16, 256, 4096])
+def test_pack_crafted_rows_nonunit_scale_exact(g):
+    """Exact rotation with a scale that is not a power of two: the float32
+    division decision must match the oracle bit for bit."""
+    k = max(g, 4096)
+    rng = np.random.default_rng(100 + g)
+    y = rng.integers(-200, 201, size=(64, k)).astype(np.float64) / 2.0  # |y| <= 100
+    y[:, 0] = 100.0
+    x = orc.rotate(y, g)
+    _say(f"pack crafted non-unit scale G={g}")
+    p = cr.pack_activations(dev(x.astype(np.float32)), g)
+    q, s = host(p.q), host(p.scale)
+    q_or, s_or = orc.pack_activations(x, g)
+    assert np.array_equal(s, s_or)
+    assert np.array_equal(q, q_or)
+
+
+@pytest.mark.parametrize("name", ["tiny_16x1024x512", "gsweep_256x4096x4096", "qkv_4096x3072x9216",
+                                  "mlp_4096x3072x12288", "video_32760x5120x13824"])
+def test_pack_parity_workloads(name):
+    w = wl.WORKLOADS[name]
+    rows = min(w.m, 512)
+    inp = wl.generate(w, m=rows)
+    x = dev(inp["x"])
+    for g in w.group_sizes:
+        _say(f"pack {name} rows={rows} G={g}")
+        p = cr.pack_activations(x, g)
+        q_or, s_or = orc.pack_activations(inp["x64"], g)
+        check_pack(host(p.q), host(p.scale), q_or, s_or, f"{name} G={g}")
+
+
+def test_pack_zero_rows_and_small_shapes():
+    rng = np.random.default_rng(3)
+    for (m, k, g) in [(1, 16, 1), (1, 16, 4), (1, 16, 16), (3, 48, 16), (5, 64, 64),
+                      (2, 1040, 16), (7, 1088, 64)]:
+        x = rng.standard_normal((m, k)).astype(np.float32)
+        x[m // 2] = 0
+        _say(f"pack small m={m} k={k} G={g}")
+        p = cr.pack_activations(dev(x), g)
+        q_or, s_or = orc.pack_activations(x.astype(np.float64), g)
+        q, s = host(p.q), host(p.scale)
+        assert s[m // 2] == 0 and np.all(q[m // 2] == 0)
+        check_pack(q, s, q_or, s_or, f"m={m} k={k} G={g}")
+
+
+@pytest.mark.parametrize("k,g,dt", [(16384, 16384, "f32"), (16384, 4096, "bf16"),
+                                     (81920, 16384, "bf16"), (131072, 16384, "f32"),
+                                     (133136, 16, "bf16"), (65536, 1024, "f32")])
+def test_pack_long_rows(k, g, dt):
+    rng = np.random.default_rng(k + g)
+    x32 = rng.standard_normal((3, k)).astype(np.float32)
+    x32[:, rng.choice(k, 5, replace=False)] *= 40
+    if dt == "bf16":
+        xt = torch.from_numpy(x32).to(torch.bfloat16)
+        x64 = xt.to(torch.float64).numpy()
+    else:
+        xt = torch.from_numpy(x32)
+        x64 = x32.astype(np.float64)
+    _say(f"pack long rows k={k} G={g} {dt}")
+    p = cr.pack_activations(xt.cuda(), g)
+    q_or, s_or = orc.pack_activations(x64, g)
+    check_pack(host(p.q), host(p.scale), q_or, s_or, f"k={k} G={g}")
+
+
+def test_pack_strided_input_and_reuse_of_output():
+    rng = np.random.default_rng(8)
+    big = rng.standard_normal((40, 2048 + 64)).astype(np.float32)
+    xt = torch.from_numpy(big).cuda()[:, :2048]  # row stride 2112 elements
+    assert xt.stride(0) == 2112
+    _say("pack strided")
+    out = cr.PackedActivation(torch.full((40, 2048), 99, dtype=torch.int8, device="cuda"),
+                              torch.full((40,), -1.0, device="cuda"), 0)
+    p = cr.pack_activations(xt, 256, out=out)
+    q_or, s_or = orc.pack_activations(big[:, :2048].astype(np.float64), 256)
+    check_pack(host(p.q), host(p.scale), q_or, s_or, "strided")
+
+
+def test_pack_is_deterministic():
+    inp = wl.generate(wl.QKV, m=256)
+    x = dev(inp["x"])
+    a = cr.pack_activations(x, 256)
+    qa, sa = host(a.q), host(a.scale)
+    b = cr.pack_activations(x, 256)
+    assert np.array_equal(qa, host(b.q)) and np.array_equal(sa, host(b.scale))
+
+
+def test_pack_leaves_input_intact():
+    inp = wl.generate(wl.TINY)
+    x = dev(inp["x"])
+    before = x.clone()
+    cr.pack_activations(x, 256)
+    torch.cuda.synchronize()
+    assert torch.equal(x, before)
+
+
+# ---------------------------------------------------------------------------
+# Weight preparation
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny_16x1024x512", "gsweep_256x4096x4096", "qkv_4096x3072x9216",
+                                  "mlp_4096x3072x12288", "video_32760x5120x13824"])
+def test_weight_prep_bit_exact(name):
+    w = wl.WORKLOADS[name]
+    inp = wl.generate(w, m=1, n_limit=2048)
+    for li, wt in enumerate(inp["weights"]):
+        for g in w.group_sizes:
+            _say(f"weights {name}[{li}] {wt.shape} G={g}")
+            qw = cr.quantize_weights(dev(wt), g)
+            q_or, s_or = orc.quantize_weights(wt, g)
+            q, s = host(qw.q), host(qw.scale)
+            assert np.array_equal(s, s_or), f"s_w differs in {np.count_nonzero(s != s_or)} rows"
+            bad = np.argwhere(q != q_or)
+            assert bad.size == 0, f"{len(bad)} Q_w codes differ, first at {bad[:4].tolist()}"
+
+
+@pytest.mark.parametrize("g", [1, 4, 64, 4096, 16384])
+def test_weight_prep_groups_and_zero_rows(g):
+    rng = np.random.default_rng(g)
+    k = max(g, 1024) * 2
+    wt = (rng.standard_normal((9, k)) * 0.02).astype(np.float32)
+    wt[4] = 0
+    _say(f"weights G={g} k={k}")
+    qw = cr.quantize_weights(dev(wt), g)
+    q_or, s_or = orc.quantize_weights(wt, g)
+    q, s = host(qw.q), host(qw.scale)
+    assert s[4] == 0 and np.all(q[4] == 0)
+    assert np.array_equal(s, s_or) and np.array_equal(q, q_or)
+
+
+# ---------------------------------------------------------------------------
+# Integer GEMM (raw int32 A)
+# ---------------------------------------------------------------------------
+
+def _raw_gemm(qx, qw, g=16):
+    px = cr.PackedActivation(dev(qx), torch.zeros(qx.shape[0], device="cuda"), g)
+    w = cr.QuantizedWeights(dev(qw), torch.zeros(qw.shape[0], device="cuda"), None, g)
+    return host(cr.linear(px, w, raw_i32=True))
+
+
+@pytest.mark.parametrize("m,k,n", [(16, 1024, 512), (256, 4096, 192), (300, 2048, 400),
+                                    (257, 3072, 193), (1, 16, 1), (33, 1040, 70),
+                                    (512, 1168, 384), (520, 3072, 3072)])
+def test_gemm_raw_int32_bit_exact(m, k, n):
+    rng = np.random.default_rng(m * 7 + n)
+    qx = rng.integers(-127, 128, size=(m, k)).astype(np.int8)
+    qw = rng.integers(-127, 128, size=(n, k)).astype(np.int8)
+    _say(f"gemm raw m={m} k={k} n={n}")
+    a = _raw_gemm(qx, qw)
+    assert np.array_equal(a.astype(np.int64), orc.int_gemm(qx, qw))
+
+
+def test_gemm_raw_int32_extremes_at_max_k():
+    k = cr.MAX_K
+    qx = np.full((2, k), 127, dtype=np.int8)
+    qx[1] = -127
+    qw = np.full((3, k), 127, dtype=np.int8)
+    qw[1] = -127
+    qw[2, ::2] = -127
+    _say("gemm raw max K")
+    a = _raw_gemm(qx, qw)
+    assert np.array_equal(a.astype(np.int64), orc.int_gemm(qx, qw))
+    assert a[0, 0] == 16129 * k
+
+
+def test_gemm_on_oracle_codes_bit_exact():
+    """The same Q_x and Q_w (from the oracle) on both sides give the same A."""
+    inp = wl.generate(wl.QKV, m=384, n_limit=960)
+    qx, _ = orc.pack_activations(inp["x64"], 256)
+    qw, _ = orc.quantize_weights(inp["weights"][0], 256)
+    _say("gemm raw on oracle codes")
+    a = _raw_gemm(qx, qw, 256)
+    assert np.array_equal(a.astype(np.int64), orc.int_gemm(qx, qw))
+
+
+# ---------------------------------------------------------------------------
+# Linear (pack + GEMM + epilogue) against the oracle
+# ---------------------------------------------------------------------------
+
+def _prep(wt, b, g):
+    return cr.quantize_weights(dev(wt), g, None if b is None else dev(b))
+
+
+@pytest.mark.parametrize("name", ["tiny_16x1024x512", "gsweep_256x4096x4096", "qkv_4096x3072x9216",
+                                  "video_32760x5120x13824"])
+def test_linear_parity(name):
+    w = wl.WORKLOADS[name]
+    rows = min(w.m, 320)
+    inp = wl.generate(w, m=rows, n_limit=1600)
+    x = dev(inp["x"])
+    for g in w.group_sizes:
+        p = cr.pack_activations(x, g)
+        qx_or, sx_or = orc.pack_activations(inp["x64"], g)
+        for li, (wt, b) in enumerate(zip(inp["weights"], inp["biases"])):
+            _say(f"linear {name}[{li}] rows={rows} n={wt.shape[0]} G={g}")
+            qw = _prep(wt, b, g)
+            y = host(cr.linear(p, qw))
+            qw_or, sw_or = orc.quantize_weights(wt, g)
+            y_or = orc.linear(qx_or, sx_or, qw_or, sw_or, b)
+            check_y(y, y_or, sx_or, sw_or, w.k, what=f"{name}[{li}] G={g}")
+
+
+def test_linear_without_bias_and_zero_weight_row():
+    inp = wl.generate(wl.TINY)
+    wt = inp["weights"][0].copy()
+    wt[7] = 0
+    b = inp["biases"][0]
+    p = cr.pack_activations(dev(inp["x"]), 256)
+    qx_or, sx_or = orc.pack_activations(inp["x64"], 256)
+    qw_or, sw_or = orc.quantize_weights(wt, 256)
+    _say("linear no bias / zero row")
+    y_nb = host(cr.linear(p, _prep(wt, None, 256)))
+    check_y(y_nb, orc.linear(qx_or, sx_or, qw_or, sw_or, None), sx_or, sw_or, 1024, what="no bias")
+    y_b = host(cr.linear(p, _prep(wt, b, 256)))
+    assert np.array_equal(y_b[:, 7], np.full(16, b[7], dtype=np.float32))  # zero row gives b
+    assert np.all(y_nb[:, 7] == 0)
+
+
+def test_linear_gelu_epilogue():
+    inp = wl.generate(wl.MLP, m=256, n_limit=1536)
+    p = cr.pack_activations(dev(inp["x"]), 256)
+    qx_or, sx_or = orc.pack_activations(inp["x64"], 256)
+    wt, b = inp["weights"][0], inp["biases"][0]
+    _say("linear gelu")
+    y = host(cr.linear(p, _prep(wt, b, 256), gelu=True))
+    qw_or, sw_or = orc.quantize_weights(wt, 256)
+    y_or = orc.linear(qx_or, sx_or, qw_or, sw_or, b, act="gelu")
+    check_y(y, y_or, sx_or, sw_or, 3072, gelu=True, what="gelu")
+
+
+def test_mlp_pair():
+    """DiT MLP: up (GELU fused) then down on the float32 GELU output."""
+    w = wl.MLP
+    rows = 256
+    inp = wl.generate(w, m=rows)
+    (w_up, w_dn), (b_up, b_dn) = inp["weights"], inp["biases"]
+    g = 256
+    # oracle chain
+    qx_or, sx_or = orc.pack_activations(inp["x64"], g)
+    qu_or, su_or = orc.quantize_weights(w_up, g)
+    h_or = orc.linear(qx_or, sx_or, qu_or, su_or, b_up, act="gelu")
+    h32 = h_or.astype(np.float32)  # the down projection's input is float32
+    qh_or, sh_or = orc.pack_activations(h32.astype(np.float64), g)
+    qd_or, sd_or = orc.quantize_weights(w_dn, g)
+    y_or = orc.linear(qh_or, sh_or, qd_or, sd_or, b_dn)
+    # device: stage by stage, each stage on the oracle's input
+    _say("mlp up")
+    up = _prep(w_up, b_up, g)
+    dn = _prep(w_dn, b_dn, g)
+    p = cr.pack_activations(dev(inp["x"]), g)
+    h = cr.linear(p, up, gelu=True)
+    check_y(host(h), h_or, sx_or, su_or, 3072, gelu=True, what="mlp up")
+    _say("mlp down on the oracle's GELU output")
+    ph = cr.pack_activations(dev(h32), g)
+    check_pack(host(ph.q), host(ph.scale), qh_or, sh_or, "mlp down pack")
+    y = host(cr.linear(ph, dn))
+    check_y(y, y_or, sh_or, sd_or, 12288, what="mlp down")
+    _say("mlp chained on device")
+    ph2 = cr.pack_activations(h, g)
+    y2 = host(cr.linear(ph2, dn))
+    check_y(y2, y_or, sh_or, sd_or, 12288, what="mlp chain")
+
+
+def test_empty_inputs():
+    x = torch.empty((0, 1024), dtype=torch.bfloat16, device="cuda")
+    p = cr.pack_activations(x, 256)
+    assert p.q.shape == (0, 1024)
+    wt = np.random.default_rng(0).standard_normal((64, 1024)).astype(np.float32)
+    qw = _prep(wt, None, 256)
+    y = cr.linear(p, qw)
+    assert y.shape == (0, 64)
+    empty_w = cr.QuantizedWeights(torch.empty((0, 1024), dtype=torch.int8, device="cuda"),
+                                  torch.empty((0,), device="cuda"), None, 256)
+    x2 = cr.pack_activations(torch.ones((4, 1024), device="cuda"), 256)
+    assert cr.linear(x2, empty_w).shape == (4, 0)
+
+
+def test_group_mismatch_raises():
+    x = cr.pack_activations(torch.ones((4, 1024), device="cuda"), 256)
+    wt = np.ones((8, 1024), dtype=np.float32)
+    qw = _prep(wt, None, 64)
+    with pytest.raises(cr.ConvrotError) as e:
+        cr.linear(x, qw)
+    assert e.value.status == cr.ERR_GROUP_MISMATCH
+
+
+# ---------------------------------------------------------------------------
+# Full sizes, in the launch configuration the benchmark times (sampled rows)
+# ---------------------------------------------------------------------------
+
+def _sample_rows(m, seed, n=48):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(m, min(m, n), replace=False).tolist()) | {0, 1, m - 2, m - 1}
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["qkv_4096x3072x9216", "mlp_4096x3072x12288",
+                                  "video_32760x5120x13824"])
+def test_full_size_sampled(name):
+    w = wl.WORKLOADS[name]
+    inp = wl.generate(w)
+    g = 256
+    rows = _sample_rows(w.m, w.seed)
+    _say(f"full {name}: pack {w.m}x{w.k}")
+    x = dev(inp["x"])
+    p = cr.pack_activations(x, g)
+    q, s = host(p.q), host(p.scale)
+    qx_or, sx_or = orc.pack_activations(inp["x64"][rows], g)
+    check_pack(q[rows], s[rows], qx_or, sx_or, f"{name} pack")
+    linears = list(zip(inp["weights"], inp["biases"]))
+    if w.gelu_chain:
+        linears = linears[:1]  # the down projection is covered by test_mlp_pair
+    for li, (wt, b) in enumerate(linears):
+        _say(f"full {name}[{li}] n={wt.shape[0]}")
+        qw = _prep(wt, b, g)
+        y = cr.linear(p, qw, gelu=w.gelu_chain)
+        yr = host(y[torch.from_numpy(rows).cuda()])
+        del y
+        qw_or, sw_or = orc.quantize_weights(wt, g)
+        assert np.array_equal(host(qw.q), qw_or) and np.array_equal(host(qw.scale), sw_or)
+        y_or = orc.linear(qx_or, sx_or, qw_or, sw_or, b, act="gelu" if w.gelu_chain else None)
+        check_y(yr, y_or, sx_or, sw_or, w.k, gelu=w.gelu_chain, what=f"{name}[{li}]")
