@@ -37,11 +37,13 @@ ACT_NONE = 0
 ACT_GELU = 1
 MAX_K = 133136
 MAX_LOG4_GROUP = 7
+MAX_GROUPED = 8
 
 EXPORTED = (
     "convrot_quantize_weights",
     "convrot_pack_activations",
     "convrot_linear",
+    "convrot_linear_grouped",
     "convrot_status_string",
     "convrot_version",
 )
@@ -95,6 +97,10 @@ def lib() -> ctypes.CDLL:
         L.convrot_linear.argtypes = [ctypes.POINTER(ConvrotPacked), ctypes.POINTER(ConvrotWeights),
                                      vp, i32, i64, i32, vp]
         L.convrot_linear.restype = ctypes.c_int
+        L.convrot_linear_grouped.argtypes = [ctypes.POINTER(ConvrotPacked),
+                                             ctypes.POINTER(ConvrotWeights), i32,
+                                             ctypes.POINTER(vp), ctypes.POINTER(i64), i32, i32, vp]
+        L.convrot_linear_grouped.restype = ctypes.c_int
         L.convrot_status_string.argtypes = [ctypes.c_int]
         L.convrot_status_string.restype = ctypes.c_char_p
         L.convrot_version.argtypes = []
@@ -124,6 +130,17 @@ def convrot_pack_activations(x, x_dtype, m, k, ldx, group_size, out: ConvrotPack
 def convrot_linear(x: ConvrotPacked, w: ConvrotWeights, y, y_dtype, ldy, act=ACT_NONE,
                    stream=None) -> int:
     return lib().convrot_linear(ctypes.byref(x), ctypes.byref(w), y, y_dtype, ldy, act, stream)
+
+
+def convrot_linear_grouped(x: ConvrotPacked, ws, ys, ldys, y_dtype, act=ACT_NONE,
+                           stream=None) -> int:
+    """ws: sequence of ConvrotWeights; ys: device pointers; ldys: row strides."""
+    n = len(ws)
+    warr = (ConvrotWeights * max(n, 1))(*ws)
+    yarr = (ctypes.c_void_p * max(n, 1))(*ys)
+    larr = (ctypes.c_int64 * max(n, 1))(*ldys)
+    return lib().convrot_linear_grouped(ctypes.byref(x), warr, n, yarr, larr, y_dtype, act,
+                                        stream)
 
 
 def convrot_version() -> int:
@@ -228,3 +245,21 @@ def linear(x: PackedActivation, w: QuantizedWeights, out: torch.Tensor | None = 
     if st != OK:
         raise ConvrotError(st, "convrot_linear")
     return out
+
+
+def linear_grouped(x: PackedActivation, ws, outs=None, raw_i32: bool = False,
+                   gelu: bool = False):
+    """Several linears on one packed activation in one launch; returns the outputs."""
+    m = x.q.shape[0]
+    dtype = torch.int32 if raw_i32 else torch.float32
+    if outs is None:
+        outs = [torch.empty((m, w.q.shape[0]), dtype=dtype, device=x.q.device) for w in ws]
+    for o in outs:
+        if o.dtype != dtype or o.dim() != 2 or o.stride(1) != 1:
+            raise ValueError("an output has the wrong dtype or layout")
+    st = convrot_linear_grouped(x.as_c(), [w.as_c() for w in ws], [_ptr(o) for o in outs],
+                                [o.stride(0) for o in outs], I32 if raw_i32 else F32,
+                                ACT_GELU if gelu else ACT_NONE, _stream())
+    if st != OK:
+        raise ConvrotError(st, "convrot_linear_grouped")
+    return outs

@@ -33,6 +33,69 @@ convrot_status from_hip(hipError_t e) { return e == hipSuccess ? CONVROT_OK : CO
 
 }  // namespace
 
+namespace {
+
+convrot_status check_out(int32_t y_dtype, int32_t act) {
+  if (y_dtype != CONVROT_F32 && y_dtype != CONVROT_I32) return CONVROT_ERR_DTYPE;
+  if (act != CONVROT_ACT_NONE && act != CONVROT_ACT_GELU) return CONVROT_ERR_DTYPE;
+  if (y_dtype == CONVROT_I32 && act != CONVROT_ACT_NONE) return CONVROT_ERR_DTYPE;
+  return CONVROT_OK;
+}
+
+// Validate one weight against the packed activation and fill its launch slot.
+convrot_status check_weight(const convrot_packed* x, const convrot_weights* w, void* y,
+                            int64_t ldy, int32_t y_dtype, convrot::GemmWeight* out) {
+  if (!w) return CONVROT_ERR_NULL;
+  if (w->k != x->k || w->group_size != x->group_size) return CONVROT_ERR_GROUP_MISMATCH;
+  if (w->n < 0 || w->n > kMaxRows || ldy < w->n) return CONVROT_ERR_SHAPE;
+  if (w->n > 0 && x->m > 0) {
+    if (!w->q || !y) return CONVROT_ERR_NULL;
+    if (y_dtype == CONVROT_F32 && !w->scale) return CONVROT_ERR_NULL;
+    // y needs only its element alignment; 16-byte rows take the vector-store path.
+    if (!aligned16(w->q) || (reinterpret_cast<uintptr_t>(y) & 3u) != 0)
+      return CONVROT_ERR_UNSUPPORTED;
+  }
+  out->qw = w->q;
+  out->sw = w->scale;
+  out->bias = w->bias;
+  out->y = y;
+  out->n = w->n;
+  out->ldy = ldy;
+  return CONVROT_OK;
+}
+
+convrot_status run_linear(const convrot_packed* x, const convrot_weights* const* w, int32_t count,
+                          void* const* y, const int64_t* ldy, int32_t y_dtype, int32_t act,
+                          void* stream) {
+  if (!x) return CONVROT_ERR_NULL;
+  int log4g = 0;
+  convrot_status st = check_k_group(x->k, x->group_size, &log4g);
+  if (st != CONVROT_OK) return st;
+  if (x->m < 0 || x->m > kMaxRows) return CONVROT_ERR_SHAPE;
+  st = check_out(y_dtype, act);
+  if (st != CONVROT_OK) return st;
+  convrot::GemmArgs a;
+  a.qx = x->q;
+  a.sx = x->scale;
+  a.m = x->m;
+  a.k = x->k;
+  a.count = 0;
+  a.raw_i32 = (y_dtype == CONVROT_I32);
+  a.gelu = (act == CONVROT_ACT_GELU);
+  for (int32_t i = 0; i < count; ++i) {
+    st = check_weight(x, w[i], y[i], ldy[i], y_dtype, &a.w[a.count]);
+    if (st != CONVROT_OK) return st;
+    if (w[i]->n > 0) ++a.count;  // empty weights launch nothing
+  }
+  if (x->m == 0 || a.count == 0) return CONVROT_OK;
+  if (!x->q) return CONVROT_ERR_NULL;
+  if (y_dtype == CONVROT_F32 && !x->scale) return CONVROT_ERR_NULL;
+  if (!aligned16(x->q)) return CONVROT_ERR_UNSUPPORTED;
+  return from_hip(convrot::launch_gemm(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* convrot_status_string(convrot_status s) {
@@ -89,35 +152,20 @@ convrot_status convrot_pack_activations(const void* x, int32_t x_dtype, int64_t 
 convrot_status convrot_linear(const convrot_packed* x, const convrot_weights* w, void* y,
                               int32_t y_dtype, int64_t ldy, int32_t act, void* stream) {
   if (!x || !w) return CONVROT_ERR_NULL;
-  int log4g = 0;
-  convrot_status st = check_k_group(x->k, x->group_size, &log4g);
-  if (st != CONVROT_OK) return st;
-  if (w->k != x->k || w->group_size != x->group_size) return CONVROT_ERR_GROUP_MISMATCH;
-  if (x->m < 0 || x->m > kMaxRows || w->n < 0 || w->n > kMaxRows) return CONVROT_ERR_SHAPE;
-  if (y_dtype != CONVROT_F32 && y_dtype != CONVROT_I32) return CONVROT_ERR_DTYPE;
-  if (act != CONVROT_ACT_NONE && act != CONVROT_ACT_GELU) return CONVROT_ERR_DTYPE;
-  if (y_dtype == CONVROT_I32 && act != CONVROT_ACT_NONE) return CONVROT_ERR_DTYPE;
-  if (ldy < w->n) return CONVROT_ERR_SHAPE;
-  if (x->m == 0 || w->n == 0) return CONVROT_OK;
-  if (!x->q || !w->q || !y) return CONVROT_ERR_NULL;
-  if (y_dtype == CONVROT_F32 && (!x->scale || !w->scale)) return CONVROT_ERR_NULL;
-  // y needs only its element alignment; 16-byte rows take the vector-store path.
-  if (!aligned16(x->q) || !aligned16(w->q) || (reinterpret_cast<uintptr_t>(y) & 3u) != 0)
-    return CONVROT_ERR_UNSUPPORTED;
-  convrot::GemmArgs a;
-  a.qx = x->q;
-  a.sx = x->scale;
-  a.qw = w->q;
-  a.sw = w->scale;
-  a.bias = w->bias;
-  a.y = y;
-  a.m = x->m;
-  a.n = w->n;
-  a.k = x->k;
-  a.ldy = ldy;
-  a.raw_i32 = (y_dtype == CONVROT_I32);
-  a.gelu = (act == CONVROT_ACT_GELU);
-  return from_hip(convrot::launch_gemm(a, static_cast<hipStream_t>(stream)));
+  const convrot_weights* ws[1] = {w};
+  void* ys[1] = {y};
+  const int64_t lds[1] = {ldy};
+  return run_linear(x, ws, 1, ys, lds, y_dtype, act, stream);
+}
+
+convrot_status convrot_linear_grouped(const convrot_packed* x, const convrot_weights* w,
+                                      int32_t count, void* const* y, const int64_t* ldy,
+                                      int32_t y_dtype, int32_t act, void* stream) {
+  if (!x || !w || !y || !ldy) return CONVROT_ERR_NULL;
+  if (count < 1 || count > CONVROT_MAX_GROUPED) return CONVROT_ERR_SHAPE;
+  const convrot_weights* ws[CONVROT_MAX_GROUPED];
+  for (int32_t i = 0; i < count; ++i) ws[i] = &w[i];
+  return run_linear(x, ws, count, y, ldy, y_dtype, act, stream);
 }
 
 }  // extern "C"

@@ -5,29 +5,37 @@
 //   A[r, o] = sum_i Q_x[r, i] Q_w[o, i]         (signed 32-bit accumulation)
 //   Y[r, o] = A[r, o] * s_x[r] * s_w[o] + b[o]
 // Both operands are int8 rows with K contiguous ("NT"), the natural operand
-// layout of the i8 MFMA instructions.
+// layout of the i8 MFMA instructions.  Several weight matrices that share one
+// packed activation (same input, same group size) run in one launch.
 //
-// Design (gfx950):
-//   * workgroup tile BM x BN (rows of Q_x x rows of Q_w), K step 128, four
-//     waves in a 2 x 2 arrangement, each owning a (BM/2) x (BN/2) block of
-//     v_mfma_i32_32x32x32_i8 accumulators (in AGPRs);
-//   * global -> LDS with direct-to-LDS 16-byte loads (no VGPR staging), double
-//     buffered: the loads of K step s+1 are spread over the MFMAs of step s;
-//   * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at slot
-//     c ^ (r & 7) ^ ((r >> 3) & 1), so the 16-byte fragment reads of 16
-//     consecutive rows hit 16 distinct bank groups;
-//   * inside a K step, every MFMA is followed by at most one LDS fragment read
-//     for the next 32-wide sub-step (two fragment register sets), with
-//     scheduling barriers pinning that order;
-//   * the MFMA takes Q_w as its first operand, so each lane ends up holding 4
-//     consecutive output columns of one output row: the fused epilogue
-//     (int32 -> float, * s_x * s_w + b, optional GELU) leaves as 16-byte
-//     stores; s_x, s_w and b of the tile are staged in LDS up front;
-//   * the epilogue mode (float, float + GELU, raw int32) is a template
-//     parameter, and interior tiles take a path without bounds checks;
-//   * workgroups are re-numbered so that each XCD (workgroups are dealt to the
-//     8 XCDs round robin) owns a contiguous band of tiles, walked in groups of
-//     a few tile rows for L2 reuse.
+// Design (gfx950), a persistent, warp-specialised kernel:
+//   * tile 256 (rows of Q_x) x 128 (rows of Q_w), K step 128 bytes;
+//   * one workgroup per CU walks a list of tiles; 8 waves per workgroup:
+//     - 4 MFMA waves (one per SIMD) each own a 128 x 64 block of
+//       v_mfma_i32_32x32x32_i8 accumulators;
+//     - 4 loader waves (one per SIMD) stream Q_x / Q_w tiles global -> LDS
+//       with direct-to-LDS 16-byte loads into a 3-stage ring, two K steps
+//       ahead and across tile boundaries, and also bring s_x, s_w and b of
+//       the next tile into a double-buffered LDS area the same way;
+//   * one s_barrier per K step hands a stage from the loaders to the MFMA
+//     waves and back.  Only the loaders wait on global loads, so the MFMA
+//     waves never wait for their own output stores: the epilogue of a tile
+//     (int32 -> float, * s_x * s_w + b, optional GELU, 16-byte stores) drains
+//     to HBM while the next tile computes;
+//   * the MFMA waves arrive at the barrier as soon as their last fragment of
+//     a stage is in registers, one 32-wide sub-step before the end of the
+//     step, and read the next stage's first fragments under that sub-step's
+//     MFMAs;
+//   * LDS rows are 128 bytes; the 16-byte chunk c of stage row r sits at slot
+//     c ^ (r & 7) ^ ((r >> 3) & 1): the 16-byte fragment reads of 16
+//     consecutive rows hit 16 distinct bank groups (no bank conflicts);
+//   * the MFMA takes Q_x as its first operand, so for each accumulator
+//     register the 32 lanes of a half-wave hold 32 consecutive output columns
+//     of one row: every 4-byte store instruction writes whole 128-byte lines;
+//   * tiles are dealt so that the workgroups on one XCD (workgroups go to
+//     the 8 XCDs round robin) share a few tile rows and columns in L2.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -36,306 +44,398 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kBK = 128;          // K bytes per step (8 chunks of 16)
-constexpr int kThreads = 256;     // 4 waves
+constexpr int kBM = 256;
+constexpr int kBN = 128;
+constexpr int kBK = 128;                              // bytes of K per step
+constexpr int kStages = 3;
+constexpr int kThreads = 512;                         // 4 MFMA + 4 loader waves
+constexpr int kStageBytes = (kBM + kBN) * kBK;        // 48 KB
+constexpr int kPieces = (kBM + kBN) / 8;              // 1 KB pieces per stage
+constexpr int kPiecesPerLoader = kPieces / 4;         // 12
+constexpr int kParFloats = kBM + 2 * kBN;             // s_x | s_w | b
+constexpr int kParBytes = kParFloats * 4;
+constexpr int kLdsBytes = kStages * kStageBytes + 2 * kParBytes;
+constexpr int kWM = kBM / 2, kWN = kBN / 2;           // MFMA wave tile 128 x 64
+constexpr int kFM = kWM / 32, kFN = kWN / 32;         // 4 x 2 MFMA blocks
 constexpr int kNumXcd = 8;
-constexpr int kDmaStride = 3;     // one direct-to-LDS load per this many MFMAs
+constexpr int kGroupM = 4;
 
 enum { kModeF32 = 0, kModeGelu = 1, kModeI32 = 2 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-CR_DEVICE void load_lds_16(const void* g, lds_void* l) {
-  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
-}
-
-struct GemmParams {
-  const int8_t* qx;
-  const float* sx;
+struct Seg {
   const int8_t* qw;
   const float* sw;
   const float* bias;
   void* y;
-  int M, N, K;
   int64_t ldy;
-  int tiles_m, group_m;
-  int vec_store;  // y 16-byte aligned and ldy % 4 == 0
+  int n;
+  int tn0;  // first global tile column of this weight
 };
 
-template <int BM, int BN>
-struct Tile {
-  static constexpr int WM = BM / 2;        // wave tile rows (Q_x)
-  static constexpr int WN = BN / 2;        // wave tile cols (Q_w)
-  static constexpr int FM = WM / 32;       // MFMA blocks along M
-  static constexpr int FN = WN / 32;       // MFMA blocks along N
-  static constexpr int A_BYTES = BM * kBK;
-  static constexpr int STAGE = (BM + BN) * kBK;
-  static constexpr int PIECES = (BM + BN) / 8;   // 1 KB pieces per stage
-  static constexpr int PIECES_PER_WAVE = PIECES / 4;
-  static_assert(PIECES % 4 == 0, "tile rows must split over 4 waves");
+struct GemmParams {
+  const int8_t* qx;
+  const float* sx;
+  int M, K, nk;
+  int nseg;
+  int tiles_m, tiles_n, total_tiles;
+  Seg seg[kMaxGemmGroup];
 };
 
-// Map the hardware workgroup id to a tile (tm, tn).
-CR_DEVICE void tile_of_block(int bid, int nblk, int tiles_m, int group_m, int& tm, int& tn) {
-  // XCD-aware renumbering: block b runs on XCD b % 8; give each XCD a contiguous range.
-  const int xcd = bid % kNumXcd;
-  const int idx = bid / kNumXcd;
-  const int q = nblk / kNumXcd, r = nblk % kNumXcd;
-  const int t = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
-  // Grouped order: walk group_m tile rows column by column.
-  const int tiles_n = nblk / tiles_m;
-  const int per_group = group_m * tiles_n;
+struct TileInfo {
+  int m0, n0, s;
+};
+
+// Tile t of the grouped order: kGroupM tile rows are walked column by column.
+CR_DEVICE TileInfo tile_info(const GemmParams& p, int t) {
+  const int per_group = kGroupM * p.tiles_n;
   const int g = t / per_group;
-  const int first = g * group_m;
-  const int gm = (tiles_m - first < group_m) ? (tiles_m - first) : group_m;
+  const int first = g * kGroupM;
+  const int gm = (p.tiles_m - first < kGroupM) ? (p.tiles_m - first) : kGroupM;
   const int in = t - g * per_group;
-  tm = first + in % gm;
-  tn = in / gm;
+  const int tm = first + in % gm;
+  const int tn = in / gm;
+  int s = 0;
+  for (int i = 1; i < p.nseg; ++i)
+    if (tn >= p.seg[i].tn0) s = i;
+  TileInfo ti;
+  ti.m0 = tm * kBM;
+  ti.n0 = (tn - p.seg[s].tn0) * kBN;
+  ti.s = s;
+  return ti;
 }
 
-// LDS slot of 16-byte chunk c in tile row r.  Rows are 128 bytes; the slot
-// permutation makes the 16-byte fragment reads of 16 consecutive rows hit 16
-// distinct 16-byte bank groups (and 8 consecutive rows 8 distinct groups).
+// Position of workgroup b inside a round of G tiles: each XCD (b % 8) gets a
+// contiguous run of tile indices.
+CR_DEVICE int round_slot(int b, int G) {
+  const int xcd = b % kNumXcd, idx = b / kNumXcd;
+  const int q = G / kNumXcd, r = G % kNumXcd;
+  return (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+}
+
 CR_DEVICE int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-CR_DEVICE v4i lds_frag(const int8_t* region, int row, int kchunk) {
-  return *reinterpret_cast<const v4i*>(region + row * kBK + ((kchunk ^ lds_swz(row)) << 4));
+CR_DEVICE v4i lds_frag(const int8_t* stage, int row, int kchunk) {
+  return *reinterpret_cast<const v4i*>(stage + row * kBK + ((kchunk ^ lds_swz(row)) << 4));
 }
 
 CR_DEVICE float gelu_erf(float y) { return 0.5f * y * (1.0f + erff(y * 0.70710678118654752f)); }
 
-template <int BM, int BN, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p) {
-  using T = Tile<BM, BN>;
-  constexpr int PPW = T::PIECES_PER_WAVE;
-  constexpr int NMF = T::FM * T::FN;       // MFMAs per 32-wide K sub-step
-  constexpr int NFR = T::FM + T::FN;       // fragment reads per sub-step
-  constexpr int KSUB = kBK / 32;           // sub-steps per K step
-  static_assert(NFR <= NMF, "fragment reads must fit between the MFMAs");
-  static_assert(PPW * kDmaStride <= NMF * KSUB, "loads must fit between the MFMAs of a K step");
-  // One LDS object holds both stages and the epilogue operands: with a second
-  // __shared__ array the compiler can no longer tell the fragment reads from
-  // the direct-to-LDS writes and puts a wait for global memory before every
-  // fragment read.
-  __shared__ __attribute__((aligned(1024))) int8_t smem[2 * T::STAGE + (BM + 2 * BN) * 4];
-  float* par = reinterpret_cast<float*>(smem + 2 * T::STAGE);  // s_x | s_w | b of the tile
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt_hi[15:14]); issued through the builtin so that the compiler's own wait
+// insertion accounts for them.
+constexpr int kWaitLgkm0 = 0xC07F;   // lgkmcnt(0)
+constexpr int kWaitVm0 = 0x0F70;     // vmcnt(0)
+constexpr int kWaitVm12 = 0x0F7C;    // vmcnt(12)
 
-  const int M = p.M, N = p.N, K = p.K;
+CR_DEVICE void barrier() {
+  // A bare s_barrier: the waits each role needs are issued explicitly, and the
+  // memory clobber keeps the compiler from moving LDS accesses across it.
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) int8_t smem[kLdsBytes];
+  int8_t* const par_base = smem + kStages * kStageBytes;
+
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  int tm, tn;
-  tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.group_m, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int G = gridDim.x;
+  const int slot = round_slot(blockIdx.x, G);
+  const int ntiles = (p.total_tiles - slot + G - 1) / G;  // tiles of this workgroup (>= 1)
+  const int nk = p.nk;
+  const int g_total = ntiles * nk;
+  const int M = p.M, K = p.K;
 
-  // Stage the epilogue operands of this tile in LDS (visible after the first
-  // barrier below).  Rows and columns past the edge read a valid neighbour;
-  // they are never stored.
-  if (MODE != kModeI32) {
-    for (int i = t; i < BM + 2 * BN; i += kThreads) {
-      float v;
-      if (i < BM) {
-        const int m = m0 + i;
-        v = p.sx[m < M ? m : M - 1];
-      } else {
-        const int c = (i < BM + BN) ? i - BM : i - BM - BN;
-        const int n = (n0 + c < N) ? n0 + c : N - 1;
-        v = (i < BM + BN) ? p.sw[n] : (p.bias ? p.bias[n] : 0.f);
+  if (wave >= 4) {
+    // ------------------------------------------------------------ loader waves
+    const int lw = wave - 4;
+    const int rip = lane >> 3;
+    // Piece q = lw + 4i covers stage rows 8q..8q+7; lane l fills slot l of it:
+    // row 8q + l/8, slot l%8, holding global 16-byte chunk (l%8) ^ swz(row).
+    int kc[kPiecesPerLoader];
+#pragma unroll
+    for (int i = 0; i < kPiecesPerLoader; ++i)
+      kc[i] = (lane & 7) ^ lds_swz((lw + 4 * i) * 8 + rip);
+
+    // The issue stream walks (tile, k step) in order; per tile it computes the
+    // source row of every piece once, so a step only adds its K offset.
+    const int8_t* rowp[kPiecesPerLoader];
+    int is_it = 0, is_ks = 0, is_stage = 0;
+    auto setup_tile = [&](int it) {
+      const TileInfo ti = tile_info(p, slot + it * G);
+      const int8_t* qw = p.seg[ti.s].qw;
+      const int n = p.seg[ti.s].n;
+#pragma unroll
+      for (int i = 0; i < kPiecesPerLoader; ++i) {
+        const int q = lw + 4 * i;
+        if (q < kBM / 8) {
+          int r = ti.m0 + q * 8 + rip;
+          r = r < M ? r : M - 1;  // rows past M load row M-1; never stored
+          rowp[i] = p.qx + (int64_t)r * K + kc[i] * 16;
+        } else {
+          int r = ti.n0 + (q - kBM / 8) * 8 + rip;
+          r = r < n ? r : n - 1;
+          rowp[i] = qw + (int64_t)r * K + kc[i] * 16;
+        }
       }
-      par[i] = v;
-    }
-  }
-
-  // Direct-to-LDS load plan: piece p (1 KB = 8 rows x 128 bytes) of a stage is
-  // loaded by wave p % 4; lane l fills LDS slot l of the piece, i.e. row
-  // 8p + l/8, slot l%8, which holds global chunk (l%8) ^ lds_swz(row).
-  const int rip = lane >> 3;
-  int kc[PPW];
-  const int8_t* row_ptr[PPW];
+    };
+    auto issue_next = [&]() {
+      if (is_ks == 0) setup_tile(is_it);
+      int8_t* stage = smem + is_stage * kStageBytes;
+      const int k0 = is_ks * kBK;
+      if (k0 + kBK <= K) {
 #pragma unroll
-  for (int i = 0; i < PPW; ++i) {
-    const int pc = wave + 4 * i;
-    kc[i] = (lane & 7) ^ lds_swz(pc * 8 + rip);
-    if (pc < BM / 8) {
-      int r = m0 + pc * 8 + rip;
-      r = r < M ? r : M - 1;  // rows past M load row M-1; never stored
-      row_ptr[i] = p.qx + (int64_t)r * K;
+        for (int i = 0; i < kPiecesPerLoader; ++i)
+          __builtin_amdgcn_global_load_lds(rowp[i] + k0, (lds_void*)(stage + (lw + 4 * i) * 1024),
+                                           16, 0, 0);
+      } else {
+        // K tail: keep every address in bounds; the chunks past K are zeroed
+        // after the loads have landed.
+#pragma unroll
+        for (int i = 0; i < kPiecesPerLoader; ++i) {
+          const int over = k0 + kc[i] * 16 - (K - 16);
+          const int8_t* src = rowp[i] + k0 - (over > 0 ? over : 0);
+          __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + (lw + 4 * i) * 1024), 16, 0, 0);
+        }
+      }
+      is_stage = (is_stage == kStages - 1) ? 0 : is_stage + 1;
+      if (++is_ks == nk) {
+        is_ks = 0;
+        ++is_it;
+      }
+    };
+    // s_x, s_w, b of tile `it` into parameter buffer it % 2 (256 lanes x 2 floats).
+    auto issue_params = [&](int it) {
+      const TileInfo ti = tile_info(p, slot + it * G);
+      const float* sw = p.seg[ti.s].sw;
+      const float* bias = p.seg[ti.s].bias;
+      const int n_lim = p.seg[ti.s].n - 1;
+      int8_t* par = par_base + (it & 1) * kParBytes;
+      const int L = lw * 64 + lane;
+      int m = ti.m0 + L;
+      m = m < M ? m : M - 1;
+      __builtin_amdgcn_global_load_lds(p.sx + m, (lds_void*)(par + lw * 256), 4, 0, 0);
+      int n = ti.n0 + (L < kBN ? L : L - kBN);
+      n = n < n_lim ? n : n_lim;
+      const float* src2 = (L < kBN || !bias) ? sw + n : bias + n;  // no bias: loaded, unused
+      __builtin_amdgcn_global_load_lds(src2, (lds_void*)(par + kBM * 4 + lw * 256), 4, 0, 0);
+    };
+    // Zero the 16-byte chunks past K of a stage (after its loads have landed).
+    auto zero_tail = [&](int stage_idx) {
+      const int k0 = (nk - 1) * kBK;
+      int8_t* stage = smem + stage_idx * kStageBytes;
+#pragma unroll
+      for (int i = 0; i < kPiecesPerLoader; ++i)
+        if (k0 + kc[i] * 16 >= K)
+          *reinterpret_cast<v4i*>(stage + (lw + 4 * i) * 1024 + lane * 16) = v4i{0, 0, 0, 0};
+    };
+    const bool ragged = (K % kBK) != 0;
+
+    issue_params(0);
+    issue_next();  // step 0
+    if (g_total > 1) {
+      issue_next();  // step 1
+      __builtin_amdgcn_s_waitcnt(kWaitVm12);  // params and step 0 landed
     } else {
-      int r = n0 + (pc - BM / 8) * 8 + rip;
-      r = r < N ? r : N - 1;
-      row_ptr[i] = p.qw + (int64_t)r * K;
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
     }
+    if (ragged && nk == 1) zero_tail(0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    barrier();  // B_0
+    int ks1 = (nk > 1) ? 1 : 0;         // k step of step g+1
+    int st1 = 1;                        // stage of step g+1
+    int pit = 1, pks = 0;               // params: tile pit is due when step g-1 opens a tile
+    for (int g = 0; g < g_total; ++g) {
+      // After B_g the MFMA waves are done reading stage (g-1) % 3 = (g+2) % 3.
+      if (g >= 1 && pks == 0 && pit < ntiles) issue_params(pit);
+      if (g >= 1 && ++pks == nk) {
+        pks = 0;
+        ++pit;
+      }
+      if (g + 2 < g_total) {
+        issue_next();  // step g+2
+        __builtin_amdgcn_s_waitcnt(kWaitVm12);  // step g+1 (and params) landed
+      } else {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      }
+      if (ragged && g + 1 < g_total && ks1 == nk - 1) zero_tail(st1);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      barrier();  // B_{g+1}
+      ks1 = (ks1 == nk - 1) ? 0 : ks1 + 1;
+      st1 = (st1 == kStages - 1) ? 0 : st1 + 1;
+    }
+    return;
   }
-  auto dma = [&](int8_t* stage, int i, int k0) {
-    int off = k0 + kc[i] * 16;
-    off = off < K - 16 ? off : K - 16;  // K tail: stay in bounds, zeroed after the wait
-    load_lds_16(row_ptr[i] + off, (lds_void*)(stage + (wave + 4 * i) * 1024));
-  };
-  auto zero_tail = [&](int8_t* stage, int k0) {
-#pragma unroll
-    for (int i = 0; i < PPW; ++i)
-      if (k0 + kc[i] * 16 >= K)
-        *reinterpret_cast<v4i*>(stage + (wave + 4 * i) * 1024 + lane * 16) = v4i{0, 0, 0, 0};
-  };
 
-  v16i acc[T::FM][T::FN];
+  // -------------------------------------------------------------- MFMA waves
+  const int wm = wave >> 1, wn = wave & 1;
+  const int frow = lane & 31;  // fragment row inside a 32-row block
+  const int fkc = lane >> 5;   // 16-byte half of a 32-byte K slice
+  v16i acc[kFM][kFN];
 #pragma unroll
-  for (int i = 0; i < T::FM; ++i)
+  for (int i = 0; i < kFM; ++i)
 #pragma unroll
-    for (int j = 0; j < T::FN; ++j) acc[i][j] = v16i{};
-
-  const int nk = (K + kBK - 1) / kBK;
-  const int frow = lane & 31;   // fragment row inside a 32-row block
-  const int fkc = lane >> 5;    // which 16-byte half of a 32-byte K slice
-  v4i xf[2][T::FM], wf[2][T::FN];
+    for (int j = 0; j < kFN; ++j) acc[i][j] = v16i{};
+  v4i xf[2][kFM], wf[2][kFN];
+  // Read slot f -> fragment, ordered as the MFMAs of a sub-step consume them:
+  // Q_x block 0, Q_w blocks 0 and 1, then Q_x blocks 1..3.
   auto read_frag = [&](const int8_t* stage, int set, int f, int kk) {
-    if (f < T::FM)
-      xf[set][f] = lds_frag(stage, wm * T::WM + f * 32 + frow, 2 * kk + fkc);
+    const bool is_x = (f == 0) || (f >= 3);
+    const int b = (f == 0) ? 0 : (f <= 2 ? f - 1 : f - 2);
+    if (is_x)
+      xf[set][b] = lds_frag(stage, wm * kWM + b * 32 + frow, 2 * kk + fkc);
     else
-      wf[set][f - T::FM] =
-          lds_frag(stage + T::A_BYTES, wn * T::WN + (f - T::FM) * 32 + frow, 2 * kk + fkc);
+      wf[set][b] = lds_frag(stage, kBM + wn * kWN + b * 32 + frow, 2 * kk + fkc);
   };
+  constexpr int NFR = kFM + kFN;  // 6 fragment reads per 32-wide sub-step
+  constexpr int NMF = kFM * kFN;  // 8 MFMAs per sub-step
 
-#pragma unroll
-  for (int i = 0; i < PPW; ++i) dma(smem, i, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if (nk == 1) zero_tail(smem, 0);
-  __syncthreads();
+  barrier();  // B_0
 #pragma unroll
   for (int f = 0; f < NFR; ++f) read_frag(smem, 0, f, 0);
 
-  for (int ks = 0; ks < nk; ++ks) {
-    int8_t* cur = smem + (ks & 1) * T::STAGE;
-    int8_t* nxt = smem + ((ks + 1) & 1) * T::STAGE;
-    // The last step re-loads its own K range into the idle buffer (never read),
-    // which keeps the loop body free of branches.
-    const int k_next = (ks + 1 < nk ? ks + 1 : ks) * kBK;
-    // One basic block: MFMAs interleaved with the fragment reads of the next
-    // sub-step and with the direct-to-LDS loads of the next K step (one per
-    // kDmaStride MFMAs: issuing them back to back stalls the MFMA stream).
+  int cur_stage = 0, ks = 0, it = 0;
+  for (int g = 0; g < g_total; ++g) {
+    const int nxt_stage = (cur_stage == kStages - 1) ? 0 : cur_stage + 1;
+    const int8_t* cur = smem + cur_stage * kStageBytes;
+    const int8_t* nxt = smem + nxt_stage * kStageBytes;
 #pragma unroll
-    for (int kk = 0; kk < KSUB; ++kk) {
+    for (int kk = 0; kk < kBK / 32; ++kk) {
       const int c = kk & 1;
 #pragma unroll
       for (int idx = 0; idx < NMF; ++idx) {
-        const int i = idx / T::FN, j = idx % T::FN;
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[c][j], xf[c][i], acc[i][j], 0, 0, 0);
+        const int i = idx / kFN, j = idx % kFN;
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf[c][i], wf[c][j], acc[i][j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        if (kk + 1 < KSUB && idx < NFR) read_frag(cur, c ^ 1, idx, kk + 1);
-        const int slot = kk * NMF + idx;
-        if (slot % kDmaStride == 0 && slot / kDmaStride < PPW) dma(nxt, slot / kDmaStride, k_next);
+        if (kk + 1 < kBK / 32 && idx < NFR) read_frag(cur, c ^ 1, idx, kk + 1);
+        if (kk == kBK / 32 - 1 && idx == 1) {
+          // Every fragment of this stage is in registers: hand the stage back
+          // (two MFMAs in flight cover the barrier), then read the next
+          // stage's first fragments under the remaining MFMAs.  After the
+          // last step this reads a stale stage of the ring: harmless, and it
+          // keeps the block free of branches.
+          __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+          barrier();  // B_{g+1}
+#pragma unroll
+          for (int f = 0; f < NFR; ++f) read_frag(nxt, 0, f, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (ks + 2 == nk) zero_tail(nxt, k_next);
-    __syncthreads();
-    if (ks + 1 < nk) {
-#pragma unroll
-      for (int f = 0; f < NFR; ++f) read_frag(nxt, 0, f, 0);
-    }
-  }
+    cur_stage = nxt_stage;
+    if (++ks < nk) continue;
+    ks = 0;
 
-  // Epilogue.  Accumulator element (i, j, r) holds output row
-  //   m = m0 + wm*WM + i*32 + (lane & 31)
-  // and output column
-  //   n = n0 + wn*WN + j*32 + 8*(r/4) + 4*(lane/32) + (r%4).
-  const bool interior = (m0 + BM <= M) && (n0 + BN <= N) && p.vec_store;
-  auto tile_value = [&](int i, int j, int g, float (&o)[4]) {
-    const int ml = wm * T::WM + i * 32 + (lane & 31);
-    const int nl = wn * T::WN + j * 32 + 8 * g + 4 * (lane >> 5);
-    const float sxm = par[ml];
-    const float4 swv = *reinterpret_cast<const float4*>(&par[BM + nl]);
-    const float4 bv = *reinterpret_cast<const float4*>(&par[BM + BN + nl]);
-    const float sv[4] = {swv.x, swv.y, swv.z, swv.w};
-    const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
+    // Epilogue of tile `it`.  Accumulator element (i, j, r) holds row
+    //   m = m0 + wm*128 + i*32 + 8*(r/4) + 4*(lane/32) + (r%4)
+    // and column
+    //   n = n0 + wn*64 + j*32 + (lane & 31).
+    const TileInfo ti = tile_info(p, slot + it * G);
+    const Seg& sg = p.seg[ti.s];
+    const float* par = reinterpret_cast<const float*>(par_base + (it & 1) * kParBytes);
+    const bool has_bias = sg.bias != nullptr;
+    const bool interior = (ti.m0 + kBM <= M) && (ti.n0 + kBN <= sg.n);
+    float swj[kFN], bj[kFN];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      float v = (float)acc[i][j][4 * g + c] * sxm;
-      v = __builtin_fmaf(v, sv[c], bb[c]);
-      if (MODE == kModeGelu) v = gelu_erf(v);
-      o[c] = v;
+    for (int j = 0; j < kFN; ++j) {
+      const int nl = wn * kWN + j * 32 + (lane & 31);
+      swj[j] = par[kBM + nl];
+      bj[j] = has_bias ? par[kBM + kBN + nl] : 0.f;
     }
-  };
-  if (interior) {
 #pragma unroll
-    for (int i = 0; i < T::FM; ++i) {
-      const int m = m0 + wm * T::WM + i * 32 + (lane & 31);
+    for (int i = 0; i < kFM; ++i) {
 #pragma unroll
-      for (int j = 0; j < T::FN; ++j) {
+      for (int rq = 0; rq < 4; ++rq) {
+        // rows ml .. ml+3 for r = 4*rq .. 4*rq+3
+        const int ml = wm * kWM + i * 32 + 8 * rq + 4 * (lane >> 5);
+        const float4 sx4 = *reinterpret_cast<const float4*>(&par[ml]);
+        const float sxr[4] = {sx4.x, sx4.y, sx4.z, sx4.w};
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * T::WN + j * 32 + 8 * g + 4 * (lane >> 5);
-          if (MODE == kModeI32) {
-            int* yr = static_cast<int*>(p.y) + (int64_t)m * p.ldy + n;
-            *reinterpret_cast<v4i*>(yr) = v4i{acc[i][j][4 * g + 0], acc[i][j][4 * g + 1],
-                                              acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-          } else {
-            float o[4];
-            tile_value(i, j, g, o);
-            float* yr = static_cast<float*>(p.y) + (int64_t)m * p.ldy + n;
-            *reinterpret_cast<float4*>(yr) = make_float4(o[0], o[1], o[2], o[3]);
+        for (int j = 0; j < kFN; ++j) {
+          const int n = ti.n0 + wn * kWN + j * 32 + (lane & 31);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int m = ti.m0 + ml + rr;
+            const int a = acc[i][j][4 * rq + rr];
+            if (MODE == kModeI32) {
+              int* yr = static_cast<int*>(sg.y) + (int64_t)m * sg.ldy + n;
+              if (interior || (m < M && n < sg.n)) *yr = a;
+            } else {
+              float v = (float)a * sxr[rr];
+              v = has_bias ? __builtin_fmaf(v, swj[j], bj[j]) : v * swj[j];
+              if (MODE == kModeGelu) v = gelu_erf(v);
+              float* yr = static_cast<float*>(sg.y) + (int64_t)m * sg.ldy + n;
+              if (interior || (m < M && n < sg.n)) *yr = v;
+            }
           }
         }
       }
     }
-  } else {
 #pragma unroll
-    for (int i = 0; i < T::FM; ++i) {
-      const int m = m0 + wm * T::WM + i * 32 + (lane & 31);
-      if (m >= M) continue;
+    for (int i = 0; i < kFM; ++i)
 #pragma unroll
-      for (int j = 0; j < T::FN; ++j) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * T::WN + j * 32 + 8 * g + 4 * (lane >> 5);
-          float o[4];
-          if (MODE != kModeI32) tile_value(i, j, g, o);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            if (n + c >= N) continue;
-            if (MODE == kModeI32)
-              static_cast<int*>(p.y)[(int64_t)m * p.ldy + n + c] = acc[i][j][4 * g + c];
-            else
-              static_cast<float*>(p.y)[(int64_t)m * p.ldy + n + c] = o[c];
-          }
-        }
-      }
-    }
+      for (int j = 0; j < kFN; ++j) acc[i][j] = v16i{};
+    ++it;
   }
 }
 
-template <int BM, int BN, int MODE>
-hipError_t launch_t(const GemmArgs& a, hipStream_t stream) {
-  GemmParams p;
-  p.qx = a.qx;
-  p.sx = a.sx;
-  p.qw = a.qw;
-  p.sw = a.sw;
-  p.bias = a.bias;
-  p.y = a.y;
-  p.M = int(a.m);
-  p.N = int(a.n);
-  p.K = int(a.k);
-  p.ldy = a.ldy;
-  p.tiles_m = int((a.m + BM - 1) / BM);
-  const int tiles_n = int((a.n + BN - 1) / BN);
-  p.group_m = 4;
-  p.vec_store = (reinterpret_cast<uintptr_t>(a.y) % 16 == 0) && (a.ldy % 4 == 0);
-  const int nblk = p.tiles_m * tiles_n;
-  hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, MODE>), dim3(nblk), dim3(kThreads), 0, stream, p);
+int device_cu_count() {
+  static std::mutex mu;
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <int MODE>
+hipError_t launch_t(const GemmParams& p, hipStream_t stream) {
+  const int cus = device_cu_count();
+  const int grid = p.total_tiles < cus ? p.total_tiles : cus;
+  hipLaunchKernelGGL((gemm_i8_kernel<MODE>), dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
-  // 256 x 192 tiles: N = 3072 gives exactly 256 tiles per 4096 rows (one per CU).
-  if (a.raw_i32) return launch_t<256, 192, kModeI32>(a, stream);
-  if (a.gelu) return launch_t<256, 192, kModeGelu>(a, stream);
-  return launch_t<256, 192, kModeF32>(a, stream);
+  GemmParams p;
+  p.qx = a.qx;
+  p.sx = a.sx;
+  p.M = int(a.m);
+  p.K = int(a.k);
+  p.nk = int((a.k + kBK - 1) / kBK);
+  p.nseg = a.count;
+  p.tiles_m = int((a.m + kBM - 1) / kBM);
+  int tn = 0;
+  for (int i = 0; i < a.count; ++i) {
+    Seg& s = p.seg[i];
+    s.qw = a.w[i].qw;
+    s.sw = a.w[i].sw;
+    s.bias = a.w[i].bias;
+    s.y = a.w[i].y;
+    s.ldy = a.w[i].ldy;
+    s.n = int(a.w[i].n);
+    s.tn0 = tn;
+    tn += int((a.w[i].n + kBN - 1) / kBN);
+  }
+  p.tiles_n = tn;
+  p.total_tiles = p.tiles_m * tn;
+  if (p.total_tiles == 0) return hipSuccess;
+  if (a.raw_i32) return launch_t<kModeI32>(p, stream);
+  if (a.gelu) return launch_t<kModeGelu>(p, stream);
+  return launch_t<kModeF32>(p, stream);
 }
 
 }  // namespace convrot

@@ -20,14 +20,22 @@ hipError_t launch_pack(const void* x, bool bf16, int64_t ldx, int64_t m, int64_t
 hipError_t launch_wprep(const float* w, int64_t n, int64_t k, int64_t ldw, int log4g,
                         int8_t* q, float* scale, hipStream_t stream);
 
-struct GemmArgs {
-  const int8_t* qx;   // [m, k]
-  const float* sx;    // [m]
+constexpr int kMaxGemmGroup = 8;  // weight matrices per grouped launch
+
+struct GemmWeight {
   const int8_t* qw;   // [n, k]
   const float* sw;    // [n]
   const float* bias;  // [n] or nullptr
   void* y;            // [m, ldy] float32 or int32
-  int64_t m, n, k, ldy;
+  int64_t n, ldy;
+};
+
+struct GemmArgs {
+  const int8_t* qx;   // [m, k]
+  const float* sx;    // [m]
+  int64_t m, k;
+  int count;          // 1 .. kMaxGemmGroup
+  GemmWeight w[kMaxGemmGroup];
   bool raw_i32;
   bool gelu;
 };

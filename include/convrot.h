@@ -50,6 +50,7 @@ extern "C" {
 
 #define CONVROT_MAX_K 133136      /* largest k with k % 16 == 0 and k*127*127 < 2^31 */
 #define CONVROT_MAX_LOG4_GROUP 7  /* group sizes 1, 4, 16, ..., 16384 */
+#define CONVROT_MAX_GROUPED 8     /* weight matrices per convrot_linear_grouped call */
 
 typedef enum convrot_status {
   CONVROT_OK = 0,
@@ -154,6 +155,23 @@ convrot_status convrot_pack_activations(const void* x, int32_t x_dtype, int64_t 
  */
 convrot_status convrot_linear(const convrot_packed* x, const convrot_weights* w, void* y,
                               int32_t y_dtype, int64_t ldy, int32_t act, void* stream);
+
+/*
+ * Several convrot linears on ONE packed activation in one launch: the linear
+ * layers that share an input and a group size reuse its packed tensor
+ * ([ICS, Runtime activation quantization]), e.g. the Q, K and V projections
+ * of an attention block.  Weight i writes y[i] (row stride ldy[i] >= w[i].n);
+ * semantics per weight are those of convrot_linear, with one y_dtype and one
+ * act for all.  Weights with n == 0 are skipped.
+ *   w   : host array of `count` convrot_weights (device pointers inside)
+ *   y   : host array of `count` device output pointers
+ *   ldy : host array of `count` row strides
+ *   1 <= count <= CONVROT_MAX_GROUPED
+ * Errors: NULL, SHAPE, GROUP_MISMATCH, DTYPE, UNSUPPORTED, HIP.
+ */
+convrot_status convrot_linear_grouped(const convrot_packed* x, const convrot_weights* w,
+                                      int32_t count, void* const* y, const int64_t* ldy,
+                                      int32_t y_dtype, int32_t act, void* stream);
 
 /* A static, human-readable name for a status code (never NULL). */
 const char* convrot_status_string(convrot_status status);

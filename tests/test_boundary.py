@@ -161,3 +161,32 @@ def test_struct_layouts_match_c():
     assert cr.ConvrotPacked.m.offset == 16 and cr.ConvrotPacked.group_size.offset == 32
     assert ctypes.sizeof(cr.ConvrotWeights) == 48
     assert cr.ConvrotWeights.n.offset == 24 and cr.ConvrotWeights.group_size.offset == 40
+
+
+def _grp(count=3, ws=None, ys=None, ldys=None, ydt=cr.F32, act=cr.ACT_NONE, gx=256, k=1024):
+    px = cr.ConvrotPacked(FAKE, FAKE, 16, k, gx)
+    if ws is None:
+        ws = [cr.ConvrotWeights(FAKE, FAKE, None, 512, k, gx) for _ in range(count)]
+    ys = [FAKE] * len(ws) if ys is None else ys
+    ldys = [w.n for w in ws] if ldys is None else ldys
+    return cr.convrot_linear_grouped(px, ws, ys, ldys, ydt, act)
+
+
+def test_linear_grouped_validation():
+    L = cr.lib()
+    assert L.convrot_linear_grouped(None, None, 1, None, None, 0, 0, None) == cr.ERR_NULL
+    assert _grp(ws=[]) == cr.ERR_SHAPE                          # count 0
+    assert _grp(count=cr.MAX_GROUPED + 1) == cr.ERR_SHAPE
+    bad_g = [cr.ConvrotWeights(FAKE, FAKE, None, 512, 1024, 256),
+             cr.ConvrotWeights(FAKE, FAKE, None, 512, 1024, 64)]
+    assert _grp(ws=bad_g) == cr.ERR_GROUP_MISMATCH              # second weight's G differs
+    bad_k = [cr.ConvrotWeights(FAKE, FAKE, None, 512, 1024, 256),
+             cr.ConvrotWeights(FAKE, FAKE, None, 512, 2048, 256)]
+    assert _grp(ws=bad_k) == cr.ERR_GROUP_MISMATCH
+    assert _grp(ldys=[512, 100, 512]) == cr.ERR_SHAPE
+    assert _grp(ys=[FAKE, None, FAKE]) == cr.ERR_NULL
+    assert _grp(ys=[FAKE, FAKE, FAKE + 2]) == cr.ERR_UNSUPPORTED
+    assert _grp(ydt=cr.BF16) == cr.ERR_DTYPE
+    assert _grp(ydt=cr.I32, act=cr.ACT_GELU) == cr.ERR_DTYPE
+    empty = [cr.ConvrotWeights(None, None, None, 0, 1024, 256) for _ in range(2)]
+    assert _grp(ws=empty, ys=[None, None], ldys=[0, 0]) == cr.OK   # nothing to launch

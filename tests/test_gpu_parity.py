@@ -306,6 +306,49 @@ def test_linear_parity(name):
             check_y(y, y_or, sx_or, sw_or, w.k, what=f"{name}[{li}] G={g}")
 
 
+@pytest.mark.parametrize("rows,ns", [(320, (3072, 3072, 3072)), (300, (1600, 200, 513)),
+                                      (16, (512,)), (1, (4, 3)), (257, (128, 256, 384, 130, 64))])
+def test_linear_grouped_parity(rows, ns):
+    """Several weights on one packed activation in one launch, against the oracle."""
+    w = wl.QKV
+    inp = wl.generate(w, m=rows, n_limit=max(ns))
+    rng = np.random.default_rng(rows + len(ns))
+    g = 256
+    p = cr.pack_activations(dev(inp["x"]), g)
+    qx_or, sx_or = orc.pack_activations(inp["x64"], g)
+    wts = [(rng.standard_normal((n, w.k)) * 0.02).astype(np.float32) for n in ns]
+    bs = [(rng.standard_normal(n) * 0.01).astype(np.float32) if i % 2 == 0 else None
+          for i, n in enumerate(ns)]
+    qws = [_prep(wt, b, g) for wt, b in zip(wts, bs)]
+    _say(f"linear grouped rows={rows} ns={ns}")
+    ys = cr.linear_grouped(p, qws)
+    for i, (wt, b) in enumerate(zip(wts, bs)):
+        qw_or, sw_or = orc.quantize_weights(wt, g)
+        y_or = orc.linear(qx_or, sx_or, qw_or, sw_or, b)
+        check_y(host(ys[i]), y_or, sx_or, sw_or, w.k, what=f"grouped[{i}]")
+    # one launch per weight gives bit-identical outputs
+    for i, q in enumerate(qws):
+        assert torch.equal(cr.linear(p, q), ys[i])
+
+
+def test_linear_grouped_raw_and_strided_outputs():
+    rng = np.random.default_rng(77)
+    k, g = 2048, 64
+    qx = rng.integers(-127, 128, size=(300, k)).astype(np.int8)
+    qws = [rng.integers(-127, 128, size=(n, k)).astype(np.int8) for n in (130, 256, 70)]
+    px = cr.PackedActivation(dev(qx), torch.zeros(300, device="cuda"), g)
+    ws = [cr.QuantizedWeights(dev(q), torch.zeros(q.shape[0], device="cuda"), None, g)
+          for q in qws]
+    # outputs as column slices of one wide buffer (row stride 470, not a multiple of 4)
+    big = torch.zeros((300, 470), dtype=torch.int32, device="cuda")
+    outs = [big[:, 0:130], big[:, 130:386], big[:, 386:456]]
+    _say("linear grouped raw int32, strided outputs")
+    cr.linear_grouped(px, ws, outs=outs, raw_i32=True)
+    for q, o in zip(qws, outs):
+        assert np.array_equal(host(o).astype(np.int64), orc.int_gemm(qx, q))
+    assert torch.count_nonzero(big[:, 456:]) == 0
+
+
 def test_linear_without_bias_and_zero_weight_row():
     inp = wl.generate(wl.TINY)
     wt = inp["weights"][0].copy()
