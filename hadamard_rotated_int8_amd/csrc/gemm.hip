@@ -8,33 +8,47 @@
 // layout of the i8 MFMA instructions.  Several weight matrices that share one
 // packed activation (same input, same group size) run in one launch.
 //
-// Design (gfx950), a persistent, warp-specialised kernel:
-//   * tile 256 (rows of Q_x) x 128 (rows of Q_w), K step 128 bytes;
-//   * one workgroup per CU walks a list of tiles; 8 waves per workgroup:
-//     - 4 MFMA waves (one per SIMD) each own a 128 x 64 block of
-//       v_mfma_i32_32x32x32_i8 accumulators;
-//     - 4 loader waves (one per SIMD) stream Q_x / Q_w tiles global -> LDS
-//       with direct-to-LDS 16-byte loads into a 3-stage ring, two K steps
-//       ahead and across tile boundaries, and also bring s_x, s_w and b of
-//       the next tile into a double-buffered LDS area the same way;
-//   * one s_barrier per K step hands a stage from the loaders to the MFMA
-//     waves and back.  Only the loaders wait on global loads, so the MFMA
-//     waves never wait for their own output stores: the epilogue of a tile
-//     (int32 -> float, * s_x * s_w + b, optional GELU, 16-byte stores) drains
-//     to HBM while the next tile computes;
-//   * the MFMA waves arrive at the barrier as soon as their last fragment of
-//     a stage is in registers, one 32-wide sub-step before the end of the
-//     step, and read the next stage's first fragments under that sub-step's
-//     MFMAs;
-//   * LDS rows are 128 bytes; the 16-byte chunk c of stage row r sits at slot
-//     c ^ (r & 7) ^ ((r >> 3) & 1): the 16-byte fragment reads of 16
-//     consecutive rows hit 16 distinct bank groups (no bank conflicts);
-//   * the MFMA takes Q_x as its first operand, so for each accumulator
-//     register the 32 lanes of a half-wave hold 32 consecutive output columns
-//     of one row: every 4-byte store instruction writes whole 128-byte lines;
-//   * tiles are dealt so that the workgroups on one XCD (workgroups go to
-//     the 8 XCDs round robin) share a few tile rows and columns in L2.
+// Design (gfx950): a persistent kernel, one workgroup of 4 waves per CU.
+//   * Output tile 256 (rows of Q_x) x BN (rows of Q_w).  Each wave (one per
+//     SIMD, so it may use the whole 512-entry register file) owns a
+//     128 x BN/2 block of v_mfma_i32_32x32x32_i8 accumulators.  When a tile
+//     is complete its accumulators are copied into a second register set and
+//     the next tile starts from zero (its first MFMAs take a zero
+//     accumulator).  The finished tile is scaled and stored a few rows per K
+//     step of the next tile (at most two groups of 2 x FN stores, one store
+//     under each odd MFMA of the middle sub-steps), so output writes are
+//     spread over the main loop instead of bursting at tile ends; the last
+//     tile of a workgroup drains after the loop.
+//   * K advances 128 bytes per step (four 32-wide sub-steps).  Operands
+//     reach LDS by direct-to-LDS buffer loads of whole 128-byte lines, one
+//     per operand row and step, through two rings: Q_x in 2 stages (loaded
+//     one step ahead), Q_w in 3 stages (two steps ahead), 145 KB with the
+//     parameter buffers.  A CU's vector-memory path moves about 64 bytes per
+//     clock, and a full-rate step needs well over half of that, so each
+//     wave's 14 loads of a step are spread one per ~3 MFMAs instead of
+//     bursting: a load that cannot issue also holds back the MFMAs behind it.
+//     The buffer resources span the tile's valid rows, so rows past M or N
+//     and chunks past K read as zero (hardware range check) and need no
+//     clamping or clearing.
+//   * One s_barrier per step, two MFMAs into the last sub-step: by then every
+//     fragment of the stage is in registers; the next stage's first fragments
+//     are read under the remaining MFMAs.
+//   * LDS rows are 128 bytes; 16-byte chunk c of stage row r sits at slot
+//     c ^ (r & 7) ^ ((r >> 3) & 1), so 16 lanes reading 16 consecutive rows
+//     touch 16 distinct groups of 4 banks.
+//   * The MFMA takes Q_x as its first operand: for each accumulator register
+//     the 32 lanes of a half-wave hold 32 consecutive columns of one output
+//     row, so every 4-byte store instruction writes whole 128-byte lines.
+//   * s_x, s_w and b of a tile reach LDS by direct-to-LDS loads two tiles
+//     ahead, in a ring of three buffers.
+//   * Loads and stores share one in-order counter (vmcnt).  Every wait names
+//     exactly the number of instructions issued after the awaited loads (this
+//     step's stores and the Q_w loads of two steps ahead).
+//   * Tiles are dealt so that the workgroups of one XCD (workgroups go to the
+//     8 XCDs round robin) work on neighbouring tile rows and columns, which
+//     they then share in that XCD's L2.
 #include <mutex>
+#include <utility>
 
 #include "common.h"
 #include "kernels.h"
@@ -44,25 +58,49 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef int v32i __attribute__((ext_vector_type(32)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBM = 256;
-constexpr int kBN = 128;
-constexpr int kBK = 128;                              // bytes of K per step
-constexpr int kStages = 3;
-constexpr int kThreads = 512;                         // 4 MFMA + 4 loader waves
-constexpr int kStageBytes = (kBM + kBN) * kBK;        // 48 KB
-constexpr int kPieces = (kBM + kBN) / 8;              // 1 KB pieces per stage
-constexpr int kPiecesPerLoader = kPieces / 4;         // 12
-constexpr int kParFloats = kBM + 2 * kBN;             // s_x | s_w | b
-constexpr int kParBytes = kParFloats * 4;
-constexpr int kLdsBytes = kStages * kStageBytes + 2 * kParBytes;
-constexpr int kWM = kBM / 2, kWN = kBN / 2;           // MFMA wave tile 128 x 64
-constexpr int kFM = kWM / 32, kFN = kWN / 32;         // 4 x 2 MFMA blocks
+constexpr int kBN = 192;       // tile columns
+constexpr int kThreads = 256;  // 4 waves
 constexpr int kNumXcd = 8;
 constexpr int kGroupM = 4;
+constexpr int kVmMax = 63;     // largest vmcnt a wait can name
+// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format).
+constexpr int kBufferWord3 = 0x00020000;
+constexpr unsigned kOutOfRange = 0x80000000u;  // an offset past every resource
 
 enum { kModeF32 = 0, kModeGelu = 1, kModeI32 = 2 };
+
+template <int BN>
+struct Cfg {
+  static constexpr int BK = 128;                          // bytes of K per step
+  static constexpr int XSTAGE = kBM * BK;                 // bytes per Q_x stage (2 stages)
+  static constexpr int WSTAGE = BN * BK;                  // bytes per Q_w stage (3 stages)
+  static constexpr int WOFF = 2 * XSTAGE;                 // LDS offset of the Q_w ring
+  static constexpr int XPW = kBM / 8 / 4;                 // 1 KB pieces (8 rows) per wave, Q_x
+  static constexpr int WPW = BN / 8 / 4;                  // ... and Q_w
+  static constexpr int XT = XPW / 2;                      // Q_x pieces issued after the barrier
+  static constexpr int WN = BN / 2;                       // wave tile columns
+  static constexpr int FM = 4, FN = WN / 32;              // 32x32 blocks per wave
+  static constexpr int NMF = FM * FN;                     // MFMAs per sub-step
+  static constexpr int NFR = FM + FN;                     // fragment reads per sub-step
+  static constexpr int PR = (kBM + 2 * BN + 255) / 256;   // parameter loads per wave and tile
+  static constexpr int PARB = PR * 256 * 4;               // bytes per parameter buffer
+  static constexpr int PAR0 = WOFF + 3 * WSTAGE;          // LDS offset of the parameter ring
+  static constexpr int LDS = PAR0 + 3 * PARB;
+  static constexpr int NG = 32;                           // store groups per tile
+  static constexpr int NV = 2 * FN;                       // values (stores) per group
+  static_assert(kBM % 32 == 0 && BN % 32 == 0, "pieces must split over 4 waves");
+  static_assert(FN >= 2 && NFR + 2 <= NMF && XT + 2 <= NMF && XPW - XT <= NMF && WPW <= 2 * NMF,
+                "interleave slots");
+  static_assert(NMF >= 2 * NV, "one store per odd slot");
+  static_assert(LDS <= 160 * 1024, "LDS");
+  static_assert(FM * FN * 16 == NG * NV, "store groups cover the tile");
+  static_assert(WPW + 2 * NV <= kVmMax, "vmcnt range");
+};
 
 struct Seg {
   const int8_t* qw;
@@ -88,6 +126,7 @@ struct TileInfo {
 };
 
 // Tile t of the grouped order: kGroupM tile rows are walked column by column.
+template <int BN>
 CR_DEVICE TileInfo tile_info(const GemmParams& p, int t) {
   const int per_group = kGroupM * p.tiles_n;
   const int g = t / per_group;
@@ -101,7 +140,7 @@ CR_DEVICE TileInfo tile_info(const GemmParams& p, int t) {
     if (tn >= p.seg[i].tn0) s = i;
   TileInfo ti;
   ti.m0 = tm * kBM;
-  ti.n0 = (tn - p.seg[s].tn0) * kBN;
+  ti.n0 = (tn - p.seg[s].tn0) * BN;
   ti.s = s;
   return ti;
 }
@@ -114,273 +153,460 @@ CR_DEVICE int round_slot(int b, int G) {
   return (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
 }
 
-CR_DEVICE int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-
-CR_DEVICE v4i lds_frag(const int8_t* stage, int row, int kchunk) {
-  return *reinterpret_cast<const v4i*>(stage + row * kBK + ((kchunk ^ lds_swz(row)) << 4));
-}
-
 CR_DEVICE float gelu_erf(float y) { return 0.5f * y * (1.0f + erff(y * 0.70710678118654752f)); }
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
-// vmcnt_hi[15:14]); issued through the builtin so that the compiler's own wait
-// insertion accounts for them.
-constexpr int kWaitLgkm0 = 0xC07F;   // lgkmcnt(0)
-constexpr int kWaitVm0 = 0x0F70;     // vmcnt(0)
-constexpr int kWaitVm12 = 0x0F7C;    // vmcnt(12)
-
 CR_DEVICE void barrier() {
-  // A bare s_barrier: the waits each role needs are issued explicitly, and the
-  // memory clobber keeps the compiler from moving LDS accesses across it.
+  // A bare s_barrier: the waits are issued explicitly, and the memory clobber
+  // keeps the compiler from moving LDS accesses across it.
   asm volatile("s_barrier" ::: "memory");
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) int8_t smem[kLdsBytes];
-  int8_t* const par_base = smem + kStages * kStageBytes;
+// s_waitcnt vmcnt(N), other counters unchanged.  gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14].
+template <int N>
+CR_DEVICE void waitvm_c() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+CR_DEVICE void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = t >> 6;
+// Wait until at most n of this wave's memory instructions are in flight,
+// where n is L plus whole store groups of NV: exact for up to two groups,
+// stricter otherwise.
+template <int L, int NV>
+CR_DEVICE void wait_younger(int n) {
+  if (n >= L + 2 * NV)
+    waitvm_c<L + 2 * NV>();
+  else if (n >= L + NV)
+    waitvm_c<L + NV>();
+  else if (n >= L)
+    waitvm_c<L>();
+  else
+    waitvm_c<0>();
+}
+
+// Slot (MFMA index in [lo, n_slots)) of the i-th of n loads spread evenly
+// over a sub-step; -1 for no load at that slot.
+constexpr int spread_piece(int idx, int lo, int n_slots, int n) {
+  for (int i = 0; i < n; ++i)
+    if (idx == lo + ((2 * i + 1) * (n_slots - lo)) / (2 * n)) return i;
+  return -1;
+}
+
+CR_DEVICE __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes,
+                                           kBufferWord3);
+}
+
+template <int BN, int MODE>
+__global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p) {
+  using C = Cfg<BN>;
+  constexpr int FM = C::FM, FN = C::FN, NV = C::NV, NG = C::NG;
+  __shared__ __attribute__((aligned(1024))) int8_t smem[C::LDS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
   const int G = gridDim.x;
   const int slot = round_slot(blockIdx.x, G);
-  const int ntiles = (p.total_tiles - slot + G - 1) / G;  // tiles of this workgroup (>= 1)
+  const int ntiles = (p.total_tiles - slot + G - 1) / G;  // >= 1: grid <= tiles
   const int nk = p.nk;
-  const int g_total = ntiles * nk;
   const int M = p.M, K = p.K;
 
-  if (wave >= 4) {
-    // ------------------------------------------------------------ loader waves
-    const int lw = wave - 4;
-    const int rip = lane >> 3;
-    // Piece q = lw + 4i covers stage rows 8q..8q+7; lane l fills slot l of it:
-    // row 8q + l/8, slot l%8, holding global 16-byte chunk (l%8) ^ swz(row).
-    int kc[kPiecesPerLoader];
-#pragma unroll
-    for (int i = 0; i < kPiecesPerLoader; ++i)
-      kc[i] = (lane & 7) ^ lds_swz((lw + 4 * i) * 8 + rip);
+  // Memory instructions (loads and counted stores) this wave has issued.
+  // Edge-tile stores are not counted: a count that is too low only makes a
+  // wait stricter.
+  int issued = 0;
 
-    // The issue stream walks (tile, k step) in order; per tile it computes the
-    // source row of every piece once, so a step only adds its K offset.
-    const int8_t* rowp[kPiecesPerLoader];
-    int is_it = 0, is_ks = 0, is_stage = 0;
-    auto setup_tile = [&](int it) {
-      const TileInfo ti = tile_info(p, slot + it * G);
-      const int8_t* qw = p.seg[ti.s].qw;
-      const int n = p.seg[ti.s].n;
-#pragma unroll
-      for (int i = 0; i < kPiecesPerLoader; ++i) {
-        const int q = lw + 4 * i;
-        if (q < kBM / 8) {
-          int r = ti.m0 + q * 8 + rip;
-          r = r < M ? r : M - 1;  // rows past M load row M-1; never stored
-          rowp[i] = p.qx + (int64_t)r * K + kc[i] * 16;
-        } else {
-          int r = ti.n0 + (q - kBM / 8) * 8 + rip;
-          r = r < n ? r : n - 1;
-          rowp[i] = qw + (int64_t)r * K + kc[i] * 16;
-        }
-      }
-    };
-    auto issue_next = [&]() {
-      if (is_ks == 0) setup_tile(is_it);
-      int8_t* stage = smem + is_stage * kStageBytes;
-      const int k0 = is_ks * kBK;
-      if (k0 + kBK <= K) {
-#pragma unroll
-        for (int i = 0; i < kPiecesPerLoader; ++i)
-          __builtin_amdgcn_global_load_lds(rowp[i] + k0, (lds_void*)(stage + (lw + 4 * i) * 1024),
-                                           16, 0, 0);
-      } else {
-        // K tail: keep every address in bounds; the chunks past K are zeroed
-        // after the loads have landed.
-#pragma unroll
-        for (int i = 0; i < kPiecesPerLoader; ++i) {
-          const int over = k0 + kc[i] * 16 - (K - 16);
-          const int8_t* src = rowp[i] + k0 - (over > 0 ? over : 0);
-          __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + (lw + 4 * i) * 1024), 16, 0, 0);
-        }
-      }
-      is_stage = (is_stage == kStages - 1) ? 0 : is_stage + 1;
-      if (++is_ks == nk) {
-        is_ks = 0;
-        ++is_it;
-      }
-    };
-    // s_x, s_w, b of tile `it` into parameter buffer it % 2 (256 lanes x 2 floats).
-    auto issue_params = [&](int it) {
-      const TileInfo ti = tile_info(p, slot + it * G);
-      const float* sw = p.seg[ti.s].sw;
-      const float* bias = p.seg[ti.s].bias;
-      const int n_lim = p.seg[ti.s].n - 1;
-      int8_t* par = par_base + (it & 1) * kParBytes;
-      const int L = lw * 64 + lane;
-      int m = ti.m0 + L;
-      m = m < M ? m : M - 1;
-      __builtin_amdgcn_global_load_lds(p.sx + m, (lds_void*)(par + lw * 256), 4, 0, 0);
-      int n = ti.n0 + (L < kBN ? L : L - kBN);
-      n = n < n_lim ? n : n_lim;
-      const float* src2 = (L < kBN || !bias) ? sw + n : bias + n;  // no bias: loaded, unused
-      __builtin_amdgcn_global_load_lds(src2, (lds_void*)(par + kBM * 4 + lw * 256), 4, 0, 0);
-    };
-    // Zero the 16-byte chunks past K of a stage (after its loads have landed).
-    auto zero_tail = [&](int stage_idx) {
-      const int k0 = (nk - 1) * kBK;
-      int8_t* stage = smem + stage_idx * kStageBytes;
-#pragma unroll
-      for (int i = 0; i < kPiecesPerLoader; ++i)
-        if (k0 + kc[i] * 16 >= K)
-          *reinterpret_cast<v4i*>(stage + (lw + 4 * i) * 1024 + lane * 16) = v4i{0, 0, 0, 0};
-    };
-    const bool ragged = (K % kBK) != 0;
-
-    issue_params(0);
-    issue_next();  // step 0
-    if (g_total > 1) {
-      issue_next();  // step 1
-      __builtin_amdgcn_s_waitcnt(kWaitVm12);  // params and step 0 landed
-    } else {
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    }
-    if (ragged && nk == 1) zero_tail(0);
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    barrier();  // B_0
-    int ks1 = (nk > 1) ? 1 : 0;         // k step of step g+1
-    int st1 = 1;                        // stage of step g+1
-    int pit = 1, pks = 0;               // params: tile pit is due when step g-1 opens a tile
-    for (int g = 0; g < g_total; ++g) {
-      // After B_g the MFMA waves are done reading stage (g-1) % 3 = (g+2) % 3.
-      if (g >= 1 && pks == 0 && pit < ntiles) issue_params(pit);
-      if (g >= 1 && ++pks == nk) {
-        pks = 0;
-        ++pit;
-      }
-      if (g + 2 < g_total) {
-        issue_next();  // step g+2
-        __builtin_amdgcn_s_waitcnt(kWaitVm12);  // step g+1 (and params) landed
-      } else {
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      }
-      if (ragged && g + 1 < g_total && ks1 == nk - 1) zero_tail(st1);
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      barrier();  // B_{g+1}
-      ks1 = (ks1 == nk - 1) ? 0 : ks1 + 1;
-      st1 = (st1 == kStages - 1) ? 0 : st1 + 1;
-    }
-    return;
-  }
-
-  // -------------------------------------------------------------- MFMA waves
-  const int wm = wave >> 1, wn = wave & 1;
-  const int frow = lane & 31;  // fragment row inside a 32-row block
-  const int fkc = lane >> 5;   // 16-byte half of a 32-byte K slice
-  v16i acc[kFM][kFN];
-#pragma unroll
-  for (int i = 0; i < kFM; ++i)
-#pragma unroll
-    for (int j = 0; j < kFN; ++j) acc[i][j] = v16i{};
-  v4i xf[2][kFM], wf[2][kFN];
-  // Read slot f -> fragment, ordered as the MFMAs of a sub-step consume them:
-  // Q_x block 0, Q_w blocks 0 and 1, then Q_x blocks 1..3.
-  auto read_frag = [&](const int8_t* stage, int set, int f, int kk) {
-    const bool is_x = (f == 0) || (f >= 3);
-    const int b = (f == 0) ? 0 : (f <= 2 ? f - 1 : f - 2);
-    if (is_x)
-      xf[set][b] = lds_frag(stage, wm * kWM + b * 32 + frow, 2 * kk + fkc);
-    else
-      wf[set][b] = lds_frag(stage, kBM + wn * kWN + b * 32 + frow, 2 * kk + fkc);
+  // ------------------------------------------------------------ loading
+  // Piece q = wave + 4i of a stage holds its rows 8q .. 8q+7.  Lane l fills
+  // LDS slot l of it: row 8q + l/8, slot l%8, which holds global chunk
+  // (l%8) ^ (row & 7) ^ ((row >> 3) & 1) = (l%8) ^ (l/8) ^ (q & 1), and
+  // q & 1 = wave & 1 for every piece of a wave.  The two operands are loaded
+  // as independent streams (Q_w runs one step further ahead); past the last
+  // tile a stream repeats that tile into stages nobody reads any more.
+  const int ld_chunk = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
+  const int ld_off = (lane >> 3) * K + ld_chunk * 16;  // < 8 * K <= 2^21
+  struct Stream {
+    __amdgpu_buffer_rsrc_t rs;
+    int it, ks, stage;
+    unsigned voff;  // this lane's offset in the current step, out of range past K
   };
-  constexpr int NFR = kFM + kFN;  // 6 fragment reads per 32-wide sub-step
-  constexpr int NMF = kFM * kFN;  // 8 MFMAs per sub-step
-
-  barrier();  // B_0
+  Stream xs{buffer_rsrc(p.qx, 0), 0, 0, 0, kOutOfRange};
+  Stream ws{buffer_rsrc(p.qx, 0), 0, 0, 0, kOutOfRange};
+  // Before the first piece of a step: the tile's buffer resource when the
+  // stream enters a new tile, and the lane offset of the step.
+  auto begin_x = [&]() {
+    if (xs.ks == 0) {
+      const TileInfo ti = tile_info<BN>(p, slot + (xs.it < ntiles ? xs.it : ntiles - 1) * G);
+      const int rows = M - ti.m0 < kBM ? M - ti.m0 : kBM;
+      xs.rs = buffer_rsrc(p.qx + (int64_t)ti.m0 * K, rows * K);
+    }
+    const int k0 = xs.ks * C::BK;
+    xs.voff = (k0 + ld_chunk * 16 < K) ? unsigned(ld_off + k0) : kOutOfRange;
+  };
+  auto begin_w = [&]() {
+    if (ws.ks == 0) {
+      const TileInfo ti = tile_info<BN>(p, slot + (ws.it < ntiles ? ws.it : ntiles - 1) * G);
+      const Seg& sg = p.seg[ti.s];
+      const int rows = sg.n - ti.n0 < BN ? sg.n - ti.n0 : BN;
+      ws.rs = buffer_rsrc(sg.qw + (int64_t)ti.n0 * K, rows * K);
+    }
+    const int k0 = ws.ks * C::BK;
+    ws.voff = (k0 + ld_chunk * 16 < K) ? unsigned(ld_off + k0) : kOutOfRange;
+  };
+  auto piece_x = [&](int i) {
+    int8_t* dst = smem + xs.stage * C::XSTAGE + (wave + 4 * i) * 1024;
+    const unsigned off = xs.voff + unsigned((wave + 4 * i) * 8 * K);
+    const __amdgpu_buffer_rsrc_t rs = xs.rs;  // (a local: the host pass rejects a member)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, off, 0, 0, 0);
+  };
+  auto piece_w = [&](int i) {
+    int8_t* dst = smem + C::WOFF + ws.stage * C::WSTAGE + (wave + 4 * i) * 1024;
+    const unsigned off = ws.voff + unsigned((wave + 4 * i) * 8 * K);
+    const __amdgpu_buffer_rsrc_t rs = ws.rs;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, off, 0, 0, 0);
+  };
+  auto end_x = [&]() {
+    issued += C::XPW;
+    xs.stage ^= 1;
+    if (++xs.ks == nk) {
+      xs.ks = 0;
+      ++xs.it;
+    }
+  };
+  auto end_w = [&]() {
+    issued += C::WPW;
+    ws.stage = ws.stage == 2 ? 0 : ws.stage + 1;
+    if (++ws.ks == nk) {
+      ws.ks = 0;
+      ++ws.it;
+    }
+  };
+  // s_x | s_w | b of tile t_it into parameter buffer t_it % 3.  Float f of a
+  // buffer is loaded by wave (f / 64) % 4, lane f % 64 (padding loads s_x[0]).
+  auto issue_params = [&](int t_it) {
+    const TileInfo ti = tile_info<BN>(p, slot + t_it * G);
+    const float* sw = p.seg[ti.s].sw;
+    const float* bias = p.seg[ti.s].bias;
+    const int n_lim = p.seg[ti.s].n - 1;
+    int8_t* par = smem + C::PAR0 + (t_it % 3) * C::PARB;
 #pragma unroll
-  for (int f = 0; f < NFR; ++f) read_frag(smem, 0, f, 0);
-
-  int cur_stage = 0, ks = 0, it = 0;
-  for (int g = 0; g < g_total; ++g) {
-    const int nxt_stage = (cur_stage == kStages - 1) ? 0 : cur_stage + 1;
-    const int8_t* cur = smem + cur_stage * kStageBytes;
-    const int8_t* nxt = smem + nxt_stage * kStageBytes;
-#pragma unroll
-    for (int kk = 0; kk < kBK / 32; ++kk) {
-      const int c = kk & 1;
-#pragma unroll
-      for (int idx = 0; idx < NMF; ++idx) {
-        const int i = idx / kFN, j = idx % kFN;
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf[c][i], wf[c][j], acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (kk + 1 < kBK / 32 && idx < NFR) read_frag(cur, c ^ 1, idx, kk + 1);
-        if (kk == kBK / 32 - 1 && idx == 1) {
-          // Every fragment of this stage is in registers: hand the stage back
-          // (two MFMAs in flight cover the barrier), then read the next
-          // stage's first fragments under the remaining MFMAs.  After the
-          // last step this reads a stale stage of the ring: harmless, and it
-          // keeps the block free of branches.
-          __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-          barrier();  // B_{g+1}
-#pragma unroll
-          for (int f = 0; f < NFR; ++f) read_frag(nxt, 0, f, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+    for (int rd = 0; rd < C::PR; ++rd) {
+      const int f0 = rd * 256 + wave * 64;
+      const int f = f0 + lane;
+      const float* src = p.sx;
+      if (f < kBM) {
+        const int m = ti.m0 + f;
+        src = p.sx + (m < M ? m : M - 1);
+      } else if (f < kBM + 2 * BN) {
+        const bool is_w = f < kBM + BN;
+        int n = ti.n0 + (is_w ? f - kBM : f - kBM - BN);
+        n = n < n_lim ? n : n_lim;
+        src = (is_w || !bias) ? sw + n : bias + n;
       }
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(par + f0 * 4), 4, 0, 0);
     }
-    cur_stage = nxt_stage;
-    if (++ks < nk) continue;
-    ks = 0;
+    issued += C::PR;
+  };
 
-    // Epilogue of tile `it`.  Accumulator element (i, j, r) holds row
-    //   m = m0 + wm*128 + i*32 + 8*(r/4) + 4*(lane/32) + (r%4)
-    // and column
-    //   n = n0 + wn*64 + j*32 + (lane & 31).
-    const TileInfo ti = tile_info(p, slot + it * G);
-    const Seg& sg = p.seg[ti.s];
-    const float* par = reinterpret_cast<const float*>(par_base + (it & 1) * kParBytes);
-    const bool has_bias = sg.bias != nullptr;
-    const bool interior = (ti.m0 + kBM <= M) && (ti.n0 + kBN <= sg.n);
-    float swj[kFN], bj[kFN];
+  // ----------------------------------------------------------- fragments
+  // Lane l reads row R + l%32 of a 32-row block (R a multiple of 32), 16-byte
+  // chunk 2*kk + l/32 of K slice kk.  Since R is a multiple of 32 the row's
+  // swizzle depends on l only, so each slice has one per-lane offset and the
+  // block adds a uniform R*128.
+  const int frow = lane & 31;
+  const int fswz = (frow & 7) ^ ((frow >> 3) & 1);
+  int fbase[4];
 #pragma unroll
-    for (int j = 0; j < kFN; ++j) {
-      const int nl = wn * kWN + j * 32 + (lane & 31);
-      swj[j] = par[kBM + nl];
-      bj[j] = has_bias ? par[kBM + kBN + nl] : 0.f;
+  for (int kk = 0; kk < 4; ++kk) fbase[kk] = frow * 128 + (((2 * kk + (lane >> 5)) ^ fswz) << 4);
+  // Q_x fragments are single-buffered: x block i is reloaded for the next
+  // sub-step right after its last MFMA (sub-steps run i-major), at least
+  // NMF - FN MFMAs before it is needed again.  Q_w fragments, used until the
+  // end of a sub-step, alternate between two sets.
+  v4i xf[FM], wf[2][FN];
+  auto read_x = [&](const int8_t* xstage, int i, int kk) {
+    xf[i] = *reinterpret_cast<const v4i*>(xstage + fbase[kk] + (wm * 128 + i * 32) * 128);
+  };
+  auto read_w = [&](const int8_t* wstage, int set, int j, int kk) {
+    wf[set][j] = *reinterpret_cast<const v4i*>(wstage + fbase[kk] + (wn * C::WN + j * 32) * 128);
+  };
+  // The fragment reads that follow MFMA idx of a sub-step, for slice kk of
+  // the given stages (the next sub-step's slice).
+  auto reads_after = [&](int idx, const int8_t* xstage, const int8_t* wstage, int kk) {
+    if (idx % FN == FN - 1) read_x(xstage, idx / FN, kk);
+    if (idx < FN) read_w(wstage, kk & 1, idx, kk);
+  };
+
+  v16i acc[FM][FN];
+
+  // ------------------------------------------------------ pending output
+  // The finished tile waits in pend: pend[e][q] is accumulator element
+  // (i, j, r) = (q / 8, e / 2, 4*((q / 2) % 4) + 2*(q % 2) + e % 2), i.e.
+  // output row pd_row0 + i*32 + 8*((q / 2) % 4) + 2*(q % 2) + e % 2 and
+  // column pd_col0 + (e / 2)*32, where pd_row0 = m0 + wm*128 + 4*(lane/32)
+  // and pd_col0 = n0 + wn*BN/2 + lane%32.  Group q holds two rows of each of
+  // the FN column blocks: NV store instructions, each writing a full
+  // 128-byte segment of two output rows.
+  v32i pend[NV];
+  int pd_valid = 0, pd_interior = 0, pd_n = 0, pd_par = C::PAR0;
+  int pd_next = 0;            // next group to store
+  int pd_due = 0, pd_rem = 0;  // groups due so far: floor(steps * NG / nk)
+  int pd_row0 = 0, pd_col0 = 0;
+  int pd_m0w = 0, pd_n0w = 0;  // uniform parts: m0 + wm*128, n0 + wn*BN/2
+  int pd_fast = 0;             // interior tile with a row stride that fits the fast path
+  unsigned pd_voff = 0;        // lane part of a fast-path store address, in bytes
+  float* pd_y = nullptr;
+  int64_t pd_ldy = 0;
+  float pd_sw[FN], pd_b[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) pd_sw[j] = pd_b[j] = 0.f;
+
+  auto group_row = [&](int q) {  // output row of element e = 0 of group q
+    return pd_row0 + (q >> 3) * 32 + 8 * ((q >> 1) & 3) + 2 * (q & 1);
+  };
+  auto read_group_sx = [&](int q) -> f32x2 {
+    return *reinterpret_cast<const f32x2*>(smem + pd_par + (group_row(q) - pd_row0 + wm * 128 +
+                                                               4 * (lane >> 5)) * 4);
+  };
+  // Value e of group q: convert, scale, store (masked on edge tiles).
+  auto store_value = [&](int q, int e, f32x2 sx, float* yrow, int m) {
+    const int j = e >> 1, rr = e & 1;
+    const int raw = pend[e][q];
+    float v;
+    if (MODE == kModeI32) {
+      v = __int_as_float(raw);
+    } else {
+      v = __builtin_fmaf((float)raw * sx[rr], pd_sw[j], pd_b[j]);
+      if (MODE == kModeGelu) v = gelu_erf(v);
     }
-#pragma unroll
-    for (int i = 0; i < kFM; ++i) {
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        // rows ml .. ml+3 for r = 4*rq .. 4*rq+3
-        const int ml = wm * kWM + i * 32 + 8 * rq + 4 * (lane >> 5);
-        const float4 sx4 = *reinterpret_cast<const float4*>(&par[ml]);
-        const float sxr[4] = {sx4.x, sx4.y, sx4.z, sx4.w};
-#pragma unroll
-        for (int j = 0; j < kFN; ++j) {
-          const int n = ti.n0 + wn * kWN + j * 32 + (lane & 31);
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const int m = ti.m0 + ml + rr;
-            const int a = acc[i][j][4 * rq + rr];
-            if (MODE == kModeI32) {
-              int* yr = static_cast<int*>(sg.y) + (int64_t)m * sg.ldy + n;
-              if (interior || (m < M && n < sg.n)) *yr = a;
-            } else {
-              float v = (float)a * sxr[rr];
-              v = has_bias ? __builtin_fmaf(v, swj[j], bj[j]) : v * swj[j];
-              if (MODE == kModeGelu) v = gelu_erf(v);
-              float* yr = static_cast<float*>(sg.y) + (int64_t)m * sg.ldy + n;
-              if (interior || (m < M && n < sg.n)) *yr = v;
-            }
-          }
-        }
-      }
+    float* yp = yrow + rr * pd_ldy + j * 32;
+    if (pd_interior) {
+      *yp = v;
+    } else if (m + rr < M && pd_col0 + j * 32 < pd_n) {
+      *yp = v;
     }
+  };
+  auto store_group = [&](int q, f32x2 sx) {
+    const int m = group_row(q);
+    float* yrow = pd_y + (int64_t)m * pd_ldy + pd_col0;
 #pragma unroll
-    for (int i = 0; i < kFM; ++i)
+    for (int e = 0; e < NV; ++e) store_value(q, e, sx, yrow, m);
+    if (pd_interior) issued += NV;
+  };
+  // On interior tiles up to two groups per K step are stored one value per
+  // odd MFMA slot of sub-steps 1 and 2 (group 0, group 1), unmasked; the
+  // address is a uniform row base plus this lane's fixed 32-bit offset
+  // (4*(lane/32) rows and lane%32 columns), and the s_x of both groups are
+  // read before the preceding barrier.  Edge tiles drain through
+  // store_group at their last step.
+  f32x2 gsx[2] = {{0.f, 0.f}, {0.f, 0.f}};
+  char* gbase[2] = {nullptr, nullptr};  // row pd_m0w + row_u(group), column pd_n0w
+  int n_grp = 0;  // groups stored during this step's sub-steps 1 and 2
+  auto group_base = [&](int q) {
+    const int row = pd_m0w + (q >> 3) * 32 + 8 * ((q >> 1) & 3) + 2 * (q & 1);
+    return reinterpret_cast<char*>(pd_y) + ((int64_t)row * pd_ldy + pd_n0w) * 4;
+  };
+  auto store_fast = [&](int q, char* base, f32x2 sx, int e) {
+    const int j = e >> 1, rr = e & 1;
+    const int raw = pend[e][q];
+    float v;
+    if (MODE == kModeI32) {
+      v = __int_as_float(raw);
+    } else {
+      v = __builtin_fmaf((float)raw * sx[rr], pd_sw[j], pd_b[j]);
+      if (MODE == kModeGelu) v = gelu_erf(v);
+    }
+    char* row = base + rr * pd_ldy * 4;
+    *reinterpret_cast<float*>(row + pd_voff + j * 128) = v;
+  };
+
+  // ------------------------------------------------------------ prologue
+  // Parameters of the first two tiles, Q_x of step 0, Q_w of steps 0 and 1;
+  // after the barrier the first Q_x pieces of step 1.
+  issue_params(0);
+  if (ntiles > 1) issue_params(1);
+  begin_x();
 #pragma unroll
-      for (int j = 0; j < kFN; ++j) acc[i][j] = v16i{};
-    ++it;
+  for (int i = 0; i < C::XPW; ++i) piece_x(i);
+  end_x();
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    begin_w();
+#pragma unroll
+    for (int i = 0; i < C::WPW; ++i) piece_w(i);
+    end_w();
   }
+  waitvm_c<0>();
+  wait_lgkm0();
+  barrier();
+#pragma unroll
+  for (int f = 0; f < FM; ++f) read_x(smem, f, 0);
+#pragma unroll
+  for (int f = 0; f < FN; ++f) read_w(smem + C::WOFF, 0, f, 0);
+  begin_x();
+#pragma unroll
+  for (int i = 0; i < C::XT; ++i) piece_x(i);
+
+  int cur_x = 0, cur_w = 0, it = 0;  // stages of the step being computed
+
+  // One K step into acc; the first step of a tile starts from zero.  Step g
+  // computes from Q_x stage g%2 and Q_w stage g%3; during it the rest of Q_x
+  // of step g+1 and all of Q_w of step g+2 are requested.
+  auto step = [&](int ks, auto first) __attribute__((always_inline)) {
+    const int8_t* cx = smem + cur_x * C::XSTAGE;
+    const int8_t* cw = smem + C::WOFF + cur_w * C::WSTAGE;
+    const int nxt_x = cur_x ^ 1, nxt_w = cur_w == 2 ? 0 : cur_w + 1;
+    const int8_t* nx = smem + nxt_x * C::XSTAGE;
+    const int8_t* nw = smem + C::WOFF + nxt_w * C::WSTAGE;
+
+    // Sub-step 0: fragments of sub-step 1, the remaining Q_x of step g+1.
+#pragma unroll
+    for (int idx = 0; idx < C::NMF; ++idx) {
+      const int i = idx / FN, j = idx % FN;
+      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+          xf[i], wf[0][j], decltype(first)::value ? v16i{} : acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      reads_after(idx, cx, cw, 1);
+      {
+        const int pc = spread_piece(idx, 0, C::NMF, C::XPW - C::XT);
+        if (pc >= 0) piece_x(C::XT + pc);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    end_x();
+    const int a_x = issued;  // after this: stores, then Q_w loads
+
+    // Groups of the pending tile due by the end of this step.
+    n_grp = 0;
+    if (pd_valid) {
+      pd_rem += NG;
+      while (pd_rem >= nk) {
+        pd_rem -= nk;
+        ++pd_due;
+      }
+      n_grp = !pd_fast ? 0 : (pd_due - pd_next < 2 ? pd_due - pd_next : 2);
+      gbase[0] = group_base(pd_next);
+      gbase[1] = group_base(pd_next + 1);
+    }
+    begin_w();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Sub-steps 1 and 2: fragments, Q_w of step g+2.
+#pragma unroll
+    for (int kk = 1; kk < 3; ++kk) {
+#pragma unroll
+      for (int idx = 0; idx < C::NMF; ++idx) {
+        const int i = idx / FN, j = idx % FN;
+        acc[i][j] =
+            __builtin_amdgcn_mfma_i32_32x32x32_i8(xf[i], wf[kk & 1][j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        reads_after(idx, cx, cw, kk + 1);
+        // Group kk-1 of this step, one value per odd slot.
+        if ((idx & 1) && idx / 2 < NV && kk - 1 < n_grp)
+          store_fast(pd_next + kk - 1, gbase[kk - 1], gsx[kk - 1], idx / 2);
+        {
+          constexpr int half = C::WPW / 2;
+          const int pc = kk == 1 ? spread_piece(idx, 0, C::NMF, half)
+                                 : spread_piece(idx, 0, C::NMF, C::WPW - half);
+          if (pc >= 0) piece_w(kk == 1 ? pc : half + pc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    end_w();
+    issued += n_grp * NV;
+    pd_next += n_grp;
+    // More than two groups per step (short K): the rest here.
+    for (; pd_next < pd_due; ++pd_next) store_group(pd_next, read_group_sx(pd_next));
+
+    // Sub-step 3: wait, barrier, fragments and first Q_x loads of the next
+    // stage.
+#pragma unroll
+    for (int idx = 0; idx < 2; ++idx) {
+      acc[0][idx] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf[0], wf[1][idx], acc[0][idx], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Q_x of step g+1 and (issued a step earlier) Q_w of step g+1 have
+    // landed once only this step's stores and Q_w loads may be in flight.
+    wait_younger<C::WPW, NV>(issued - a_x);
+    // s_x of the next step's two groups, complete at the wait below.
+    gsx[0] = read_group_sx(pd_next < NG ? pd_next : NG - 1);
+    gsx[1] = read_group_sx(pd_next + 1 < NG ? pd_next + 1 : NG - 1);
+    wait_lgkm0();
+    barrier();  // the next stages are readable by all, this step's are free
+    if (ks == nk - 1 && it + 2 < ntiles) issue_params(it + 2);
+    begin_x();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int idx = 2; idx < C::NMF; ++idx) {
+      const int i = idx / FN, j = idx % FN;
+      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf[i], wf[1][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // After the barrier: x block 0 (free since MFMA 2) and the Q_w set of
+      // the next step's first sub-step, then x blocks as they free up.
+      if (idx % FN == FN - 1) read_x(nx, idx / FN, 0);
+      if (idx >= 2 && idx < 2 + FN) read_w(nw, 0, idx - 2, 0);
+      {
+        const int pc = spread_piece(idx, 2, C::NMF, C::XT);
+        if (pc >= 0) piece_x(pc);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    cur_x = nxt_x;
+    cur_w = nxt_w;
+  };
+
+  for (it = 0; it < ntiles; ++it) {
+    step(0, std::true_type{});
+    for (int ks = 1; ks < nk; ++ks) step(ks, std::false_type{});
+
+    // The tile is complete and the previous one fully stored: move the
+    // accumulators into pend.  The tile's parameters were requested two
+    // tiles ago and have been waited for since.
+#pragma unroll
+    for (int q = 0; q < NG; ++q)
+#pragma unroll
+      for (int e = 0; e < NV; ++e)
+        pend[e][q] = acc[q >> 3][e >> 1][4 * ((q >> 1) & 3) + 2 * (q & 1) + (e & 1)];
+    const TileInfo ti = tile_info<BN>(p, slot + it * G);
+    const Seg& sg = p.seg[ti.s];
+    pd_valid = 1;
+    pd_next = 0;
+    pd_due = 0;
+    pd_rem = 0;
+    pd_par = C::PAR0 + (it % 3) * C::PARB;
+    pd_row0 = ti.m0 + wm * 128 + 4 * (lane >> 5);
+    pd_col0 = ti.n0 + wn * C::WN + (lane & 31);
+    pd_y = static_cast<float*>(sg.y);
+    pd_ldy = sg.ldy;
+    pd_n = sg.n;
+    pd_interior = (ti.m0 + kBM <= M) && (ti.n0 + BN <= sg.n);
+    pd_m0w = ti.m0 + wm * 128;
+    pd_n0w = ti.n0 + wn * C::WN;
+    pd_fast = pd_interior && sg.ldy < (int64_t(1) << 26);
+    pd_voff = unsigned((4 * (lane >> 5)) * (int)(pd_fast ? sg.ldy : 0) + (lane & 31)) * 4u;
+    gsx[0] = read_group_sx(0);
+    gsx[1] = read_group_sx(1);
+    const float* par = reinterpret_cast<const float*>(smem + pd_par);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int nl = wn * C::WN + j * 32 + (lane & 31);
+      pd_sw[j] = par[kBM + nl];
+      pd_b[j] = sg.bias ? par[kBM + BN + nl] : 0.f;
+    }
+  }
+  // The last tile.
+  if (pd_fast) {
+    for (; pd_next < NG; ++pd_next) {
+      const f32x2 sx = read_group_sx(pd_next);
+      char* base = group_base(pd_next);
+#pragma unroll
+      for (int e = 0; e < NV; ++e) store_fast(pd_next, base, sx, e);
+    }
+  } else {
+    for (; pd_next < NG; ++pd_next) store_group(pd_next, read_group_sx(pd_next));
+  }
+  waitvm_c<0>();         // no load into LDS may still be in flight at exit
 }
 
 int device_cu_count() {
@@ -399,26 +625,33 @@ int device_cu_count() {
   return cus[dev];
 }
 
-template <int MODE>
-hipError_t launch_t(const GemmParams& p, hipStream_t stream) {
+template <int BN, int MODE>
+hipError_t launch_t(GemmParams p, hipStream_t stream) {
+  p.tiles_m = (p.M + kBM - 1) / kBM;
+  int tn = 0;
+  for (int i = 0; i < p.nseg; ++i) {
+    p.seg[i].tn0 = tn;
+    tn += (p.seg[i].n + BN - 1) / BN;
+  }
+  p.tiles_n = tn;
+  p.total_tiles = p.tiles_m * tn;
+  p.nk = (p.K + Cfg<BN>::BK - 1) / Cfg<BN>::BK;
+  if (p.total_tiles == 0) return hipSuccess;
   const int cus = device_cu_count();
   const int grid = p.total_tiles < cus ? p.total_tiles : cus;
-  hipLaunchKernelGGL((gemm_i8_kernel<MODE>), dim3(grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((gemm_i8_kernel<BN, MODE>), dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
-  GemmParams p;
+  GemmParams p{};
   p.qx = a.qx;
   p.sx = a.sx;
   p.M = int(a.m);
   p.K = int(a.k);
-  p.nk = int((a.k + kBK - 1) / kBK);
   p.nseg = a.count;
-  p.tiles_m = int((a.m + kBM - 1) / kBM);
-  int tn = 0;
   for (int i = 0; i < a.count; ++i) {
     Seg& s = p.seg[i];
     s.qw = a.w[i].qw;
@@ -427,15 +660,11 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     s.y = a.w[i].y;
     s.ldy = a.w[i].ldy;
     s.n = int(a.w[i].n);
-    s.tn0 = tn;
-    tn += int((a.w[i].n + kBN - 1) / kBN);
+    s.tn0 = 0;
   }
-  p.tiles_n = tn;
-  p.total_tiles = p.tiles_m * tn;
-  if (p.total_tiles == 0) return hipSuccess;
-  if (a.raw_i32) return launch_t<kModeI32>(p, stream);
-  if (a.gelu) return launch_t<kModeGelu>(p, stream);
-  return launch_t<kModeF32>(p, stream);
+  if (a.raw_i32) return launch_t<kBN, kModeI32>(p, stream);
+  if (a.gelu) return launch_t<kBN, kModeGelu>(p, stream);
+  return launch_t<kBN, kModeF32>(p, stream);
 }
 
 }  // namespace convrot

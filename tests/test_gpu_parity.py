@@ -256,6 +256,20 @@ def test_gemm_raw_int32_bit_exact(m, k, n):
     assert np.array_equal(a.astype(np.int64), orc.int_gemm(qx, qw))
 
 
+@pytest.mark.parametrize("m,k,n", [(4096, 256, 8192), (2304, 80, 8320), (1100, 16, 9000),
+                                    (1300, 1040, 6500)])
+def test_gemm_raw_int32_many_tiles_per_workgroup(m, k, n):
+    """More output tiles than compute units: each workgroup walks several
+    tiles, with loads running ahead across tile boundaries (also for one- and
+    two-step K, and ragged M, N and K)."""
+    rng = np.random.default_rng(m + k + n)
+    qx = rng.integers(-127, 128, size=(m, k)).astype(np.int8)
+    qw = rng.integers(-127, 128, size=(n, k)).astype(np.int8)
+    _say(f"gemm raw many tiles m={m} k={k} n={n}")
+    a = _raw_gemm(qx, qw)
+    assert np.array_equal(a.astype(np.int64), orc.int_gemm(qx, qw))
+
+
 def test_gemm_raw_int32_extremes_at_max_k():
     k = cr.MAX_K
     qx = np.full((2, k), 127, dtype=np.int8)
@@ -329,6 +343,23 @@ def test_linear_grouped_parity(rows, ns):
     # one launch per weight gives bit-identical outputs
     for i, q in enumerate(qws):
         assert torch.equal(cr.linear(p, q), ys[i])
+
+
+@pytest.mark.parametrize("m,n,gelu", [(1100, 9000, False), (1300, 6500, True)])
+def test_linear_many_tiles_per_workgroup(m, n, gelu):
+    """Scaled output of every element when workgroups walk several tiles."""
+    rng = np.random.default_rng(m + n)
+    k, g = 1024, 256
+    x = (rng.standard_normal((m, k)) * 0.5).astype(np.float32)
+    wt = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    b = (rng.standard_normal(n) * 0.01).astype(np.float32)
+    _say(f"linear many tiles m={m} n={n} gelu={gelu}")
+    p = cr.pack_activations(dev(x), g)
+    y = host(cr.linear(p, _prep(wt, b, g), gelu=gelu))
+    qx_or, sx_or = orc.pack_activations(x.astype(np.float64), g)
+    qw_or, sw_or = orc.quantize_weights(wt, g)
+    y_or = orc.linear(qx_or, sx_or, qw_or, sw_or, b, act="gelu" if gelu else None)
+    check_y(y, y_or, sx_or, sw_or, k, gelu=gelu, what=f"many tiles {m}x{n}")
 
 
 def test_linear_grouped_raw_and_strided_outputs():
