@@ -25,6 +25,14 @@
 //   * the code decision is made in float32: s = m/127 (IEEE division), then
 //     v = RN(x/s) via a correctly rounded reciprocal plus one FMA correction,
 //     then round-half-away; the int8 codes leave as 16-byte stores.
+//
+// Fast path (pack_rows_kernel), used when G <= 1024 and K is a multiple of
+// 1024 (every row then splits into whole 64-chunk wave loads): one wave owns
+// one row, lane l holds chunks c*64 + l (c < K/1024) with the same lane
+// permutation, so all digits live in registers, DPP and lane shuffles; the
+// absmax is a wave reduction.  No LDS and no barriers: a workgroup is just
+// four independent rows, and every row of the matrix can be in flight at
+// once, which is what an HBM-bound pass needs.
 #include "common.h"
 #include "kernels.h"
 
@@ -275,6 +283,289 @@ __global__ __launch_bounds__(1024) void pack_kernel(const InT* __restrict__ x, i
   }
 }
 
+// ---- fast path helpers: the same transforms in forms that need no register
+// copies (every instruction writes a fresh value or folds its lane exchange).
+
+// 2 * H4 on four registers: y_i = S - 2 x_{3-i} with S = (a+b)+(c+d), the
+// four products as three-operand FMAs (the two-operand accumulating form
+// would need a copy of S for each output).
+CR_DEVICE float fma_m2(float x, float s) {
+  float y;
+  asm("v_fma_f32 %0, %1, -2.0, %2" : "=v"(y) : "v"(x), "v"(s));
+  return y;
+}
+CR_DEVICE void h4_reg_pq(float& a, float& b, float& c, float& d) {
+  const float s = (a + b) + (c + d);
+  const float y0 = fma_m2(d, s), y1 = fma_m2(c, s), y2 = fma_m2(b, s), y3 = fma_m2(a, s);
+  a = y0;
+  b = y1;
+  c = y2;
+  d = y3;
+}
+
+template <int kCtrl>
+CR_DEVICE float lane_mov(float v) {  // lane exchange that folds into its user
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, true));
+}
+
+// Lane digits: y = S - 2 x_rev with S the sum over the digit's four lanes;
+// m2 holds -2 in a register so the last step is one fmac with a lane operand.
+CR_DEVICE float h4_quad_f(float x, float m2) {
+  const float t = x + lane_mov<kDppQuadSwap1>(x);
+  const float s = t + lane_mov<kDppQuadSwap2>(t);
+  return __builtin_fmaf(lane_mov<kDppQuadRev>(x), m2, s);
+}
+CR_DEVICE float h4_row_f(float x, float m2) {
+  const float t = x + lane_mov<kDppRowRor4>(x);
+  const float s = t + lane_mov<kDppRowRor8>(t);
+  return __builtin_fmaf(lane_mov<kDppRowRor8>(x), m2, s);
+}
+
+CR_DEVICE void rotate_fast(float* v, int log4g, float m2) {
+  if (log4g >= 1) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) h4_reg_pq(v[4 * a], v[4 * a + 1], v[4 * a + 2], v[4 * a + 3]);
+  }
+  if (log4g >= 2) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) h4_reg_pq(v[a], v[a + 4], v[a + 8], v[a + 12]);
+  }
+  if (log4g >= 3) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = h4_quad_f(v[e], m2);
+  }
+  if (log4g >= 4) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = h4_row_f(v[e], m2);
+  }
+  if (log4g >= 5) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = h4_wave(v[e]);
+  }
+}
+
+// Four clamped codes (low bytes of a, b, c, d) into one word.
+CR_DEVICE uint32_t pack4_perm(int a, int b, int c, int d) {
+  const uint32_t lo = __builtin_amdgcn_perm(uint32_t(b), uint32_t(a), 0x0c0c0400u);  // [a0 b0 0 0]
+  const uint32_t hi = __builtin_amdgcn_perm(uint32_t(d), uint32_t(c), 0x04000c0cu);  // [0 0 c0 d0]
+  return lo | hi;
+}
+
+template <typename InT>
+struct RawChunk;  // one chunk (16 features) as loaded
+template <>
+struct RawChunk<uint16_t> {
+  u32x4 w[2];
+  CR_DEVICE void load(const uint16_t* p) {
+    const u32x4* p4 = reinterpret_cast<const u32x4*>(p);
+    w[0] = __builtin_nontemporal_load(p4);
+    w[1] = __builtin_nontemporal_load(p4 + 1);
+  }
+  CR_DEVICE void unpack(float* v) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      v[8 * i + 0] = bf16_lo(w[i].x);
+      v[8 * i + 1] = bf16_hi(w[i].x);
+      v[8 * i + 2] = bf16_lo(w[i].y);
+      v[8 * i + 3] = bf16_hi(w[i].y);
+      v[8 * i + 4] = bf16_lo(w[i].z);
+      v[8 * i + 5] = bf16_hi(w[i].z);
+      v[8 * i + 6] = bf16_lo(w[i].w);
+      v[8 * i + 7] = bf16_hi(w[i].w);
+    }
+  }
+};
+template <>
+struct RawChunk<float> {
+  f32x4 w[4];
+  CR_DEVICE void load(const float* p) {
+    const f32x4* p4 = reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = __builtin_nontemporal_load(p4 + i);
+  }
+  CR_DEVICE void unpack(float* v) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[4 * i + 0] = w[i].x;
+      v[4 * i + 1] = w[i].y;
+      v[4 * i + 2] = w[i].z;
+      v[4 * i + 3] = w[i].w;
+    }
+  }
+};
+
+// One wave per row at a time; a wave walks rows row0, row0 + W, ... (W waves
+// in the grid) and loads the next row while it transforms the current one.
+template <typename InT, int CPL>
+__global__ __launch_bounds__(256) void pack_rows_kernel(const InT* __restrict__ x, int64_t ldx,
+                                                        int m, int k, int log4g,
+                                                        int8_t* __restrict__ q,
+                                                        float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int nw = gridDim.x * 4;
+  int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= m) return;  // the whole wave: no barriers below
+  const int lp = chunk_of_thread(lane);
+  float m2;
+  asm volatile("v_mov_b32 %0, -2.0" : "=v"(m2));  // -2 in a register (see h4_quad_f)
+  RawChunk<InT> raw[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) raw[c].load(x + (int64_t)row * ldx + (int64_t)(c * 64 + lp) * 16);
+  for (; row < m; row += nw) {
+    float v[CPL][16];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) raw[c].unpack(v[c]);
+    const int nrow = row + nw;
+    if (nrow < m) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        raw[c].load(x + (int64_t)nrow * ldx + (int64_t)(c * 64 + lp) * 16);
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) rotate_fast(v[c], log4g, m2);
+    float mx = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(v[c][e]));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    // Undo the unnormalised butterfly's exact factor 2^n, then s = max / 127.
+    const float s = ldexpf(mx, -log4g) / 127.0f;
+    if (lane == 0) scale[row] = s;
+    const float s_un = ldexpf(s, log4g);  // x_un / s_un == x / s exactly
+    const float r = (s_un != 0.f) ? 1.0f / s_un : 0.f;
+    int8_t* qr = q + (int64_t)row * k;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      int qi[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        qi[e] = s_un != 0.f ? clamp127(round_half_away_small(div_by_recip(v[c][e], s_un, r))) : 0;
+      uint4 o;
+      o.x = pack4_perm(qi[0], qi[1], qi[2], qi[3]);
+      o.y = pack4_perm(qi[4], qi[5], qi[6], qi[7]);
+      o.z = pack4_perm(qi[8], qi[9], qi[10], qi[11]);
+      o.w = pack4_perm(qi[12], qi[13], qi[14], qi[15]);
+      *reinterpret_cast<uint4*>(qr + (int64_t)(c * 64 + lp) * 16) = o;
+    }
+  }
+}
+
+// G = 64 and 256: the digits held by lane bits 0-3 are brought into registers
+// by a 16 x 16 transpose through LDS inside each group of 16 lanes, so every
+// butterfly stage is a register stage (two adds per element) and the lane
+// exchange is LDS traffic instead of VALU work.  The codes are then stored
+// one byte per lane from the transposed layout (16 consecutive bytes per
+// group of 16 lanes): no packing.  A row's maximum satisfies |x| <= max, so
+// |x / s| <= 127 (1 + 2^-23) and the code needs no clamp.
+constexpr int kTStride = 272;  // floats per 16-lane group: 256 + 16 (bank offset)
+
+template <typename InT, int CPL>
+__global__ __launch_bounds__(256) void pack_rows_lds_kernel(const InT* __restrict__ x,
+                                                            int64_t ldx, int m, int k,
+                                                            int log4g, int8_t* __restrict__ q,
+                                                            float* __restrict__ scale) {
+  __shared__ __attribute__((aligned(16))) float tbuf[4][4 * kTStride];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int grp = lane >> 4, li = lane & 15;
+  const int nw = gridDim.x * 4;
+  int row = blockIdx.x * 4 + wv;
+  if (row >= m) return;  // the whole wave: no barriers below
+  float* tw = &tbuf[wv][grp * kTStride];
+  RawChunk<InT> raw[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) raw[c].load(x + (int64_t)row * ldx + (int64_t)(c * 64 + lane) * 16);
+  for (; row < m; row += nw) {
+    // t[c][i] = element li of chunk c*64 + 16*grp + i, after the transpose
+    float t[CPL][16];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      float v[16];
+      raw[c].unpack(v);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) h4_reg_pq(v[4 * a], v[4 * a + 1], v[4 * a + 2], v[4 * a + 3]);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) h4_reg_pq(v[a], v[a + 4], v[a + 8], v[a + 12]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<f32x4*>(tw + li * 16 + 4 * i) =
+            f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) t[c][i] = tw[i * 16 + li];
+    }
+    const int nrow = row + nw;
+    if (nrow < m) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        raw[c].load(x + (int64_t)nrow * ldx + (int64_t)(c * 64 + lane) * 16);
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) h4_reg_pq(t[c][4 * a], t[c][4 * a + 1], t[c][4 * a + 2], t[c][4 * a + 3]);
+      if (log4g >= 4) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) h4_reg_pq(t[c][a], t[c][a + 4], t[c][a + 8], t[c][a + 12]);
+      }
+    }
+    float mx = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(t[c][e]));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float s = ldexpf(mx, -log4g) / 127.0f;
+    if (lane == 0) scale[row] = s;
+    const float s_un = ldexpf(s, log4g);
+    const float r = (s_un != 0.f) ? 1.0f / s_un : 0.f;
+    int8_t* qr = q + (int64_t)row * k + (16 * grp) * 16 + li;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int code = s_un != 0.f ? round_half_away_small(div_by_recip(t[c][i], s_un, r)) : 0;
+        qr[(c * 64 + i) * 16] = (int8_t)code;
+      }
+  }
+}
+
+template <typename InT, int CPL>
+hipError_t launch_rows_t(const void* x, int64_t ldx, int m, int k, int log4g, int8_t* q,
+                         float* scale, hipStream_t stream) {
+  // One row per wave up to 16 waves per CU (8 for rows of more than three
+  // chunks per lane, whose registers allow no more); beyond that each wave
+  // walks several rows, loading the next while it transforms the current one.
+  const int cap = 256 * (CPL <= 3 ? 16 : 8);
+  const int waves = m < cap ? m : cap;
+  const int grid = (waves + 3) / 4;
+  if (log4g == 3 || log4g == 4)
+    hipLaunchKernelGGL((pack_rows_lds_kernel<InT, CPL>), dim3(grid), dim3(256), 0, stream,
+                       static_cast<const InT*>(x), ldx, m, k, log4g, q, scale);
+  else
+    hipLaunchKernelGGL((pack_rows_kernel<InT, CPL>), dim3(grid), dim3(256), 0, stream,
+                       static_cast<const InT*>(x), ldx, m, k, log4g, q, scale);
+  return hipGetLastError();
+}
+
+template <typename InT>
+hipError_t launch_rows(const void* x, int64_t ldx, int m, int k, int log4g, int8_t* q,
+                       float* scale, hipStream_t stream) {
+  switch (k / 1024) {
+    case 1: return launch_rows_t<InT, 1>(x, ldx, m, k, log4g, q, scale, stream);
+    case 2: return launch_rows_t<InT, 2>(x, ldx, m, k, log4g, q, scale, stream);
+    case 3: return launch_rows_t<InT, 3>(x, ldx, m, k, log4g, q, scale, stream);
+    case 4: return launch_rows_t<InT, 4>(x, ldx, m, k, log4g, q, scale, stream);
+    case 5: return launch_rows_t<InT, 5>(x, ldx, m, k, log4g, q, scale, stream);
+    case 6: return launch_rows_t<InT, 6>(x, ldx, m, k, log4g, q, scale, stream);
+    case 7: return launch_rows_t<InT, 7>(x, ldx, m, k, log4g, q, scale, stream);
+    case 8: return launch_rows_t<InT, 8>(x, ldx, m, k, log4g, q, scale, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename InT, int CPT>
 hipError_t launch_pack_t(const void* x, int64_t ldx, int m, int k, int log4g, int threads,
                          int nseg, int8_t* q, float* scale, hipStream_t stream) {
@@ -312,8 +603,12 @@ PackPlan plan_pack(int64_t k) {
 
 hipError_t launch_pack(const void* x, bool bf16, int64_t ldx, int64_t m, int64_t k, int log4g,
                        int8_t* q, float* scale, hipStream_t stream) {
-  const PackPlan p = plan_pack(k);
   const int mi = int(m), ki = int(k);
+  if (log4g <= 5 && k % 1024 == 0 && k / 1024 <= 8) {
+    return bf16 ? launch_rows<uint16_t>(x, ldx, mi, ki, log4g, q, scale, stream)
+                : launch_rows<float>(x, ldx, mi, ki, log4g, q, scale, stream);
+  }
+  const PackPlan p = plan_pack(k);
   switch (p.chunks_per_thread * 2 + (bf16 ? 1 : 0)) {
     case 2: return launch_pack_t<float, 1>(x, ldx, mi, ki, log4g, p.threads, p.segments, q, scale, stream);
     case 3: return launch_pack_t<uint16_t, 1>(x, ldx, mi, ki, log4g, p.threads, p.segments, q, scale, stream);
