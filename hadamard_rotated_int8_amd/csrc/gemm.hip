@@ -13,23 +13,27 @@
 //     SIMD, so it may use the whole 512-entry register file) owns a
 //     128 x BN/2 block of v_mfma_i32_32x32x32_i8 accumulators.  When a tile
 //     is complete its accumulators are copied into a second register set and
-//     the next tile starts from zero (its first MFMAs take a zero
-//     accumulator).  The finished tile is scaled and stored a few rows per K
-//     step of the next tile (at most two groups of 2 x FN stores, one store
-//     under each odd MFMA of the middle sub-steps), so output writes are
-//     spread over the main loop instead of bursting at tile ends; the last
-//     tile of a workgroup drains after the loop.
+//     the next tile starts from zero.
+//   * The finished tile is scaled and stored during the first 16 K steps of
+//     the next tile, two fixed groups of 2 x FN values per step, one store
+//     under each odd MFMA of the middle sub-steps.  Those 16 steps are
+//     unrolled, so every store names its registers at compile time and the
+//     K loop carries no store bookkeeping.  Output writes are thus spread over
+//     the main loop instead of bursting at tile ends.
 //   * K advances 128 bytes per step (four 32-wide sub-steps).  Operands
 //     reach LDS by direct-to-LDS buffer loads of whole 128-byte lines, one
 //     per operand row and step, through two rings: Q_x in 2 stages (loaded
-//     one step ahead), Q_w in 3 stages (two steps ahead), 145 KB with the
-//     parameter buffers.  A CU's vector-memory path moves about 64 bytes per
-//     clock, and a full-rate step needs well over half of that, so each
-//     wave's 14 loads of a step are spread one per ~3 MFMAs instead of
-//     bursting: a load that cannot issue also holds back the MFMAs behind it.
-//     The buffer resources span the tile's valid rows, so rows past M or N
-//     and chunks past K read as zero (hardware range check) and need no
-//     clamping or clearing.
+//     one step ahead), Q_w in 3 stages (two steps ahead).  Each wave's 14
+//     loads of a step are spread one per ~3 MFMAs: a load that cannot issue
+//     also holds back the MFMAs behind it.  The buffer resources span the
+//     tile's valid rows, so rows past M or N and chunks past K read as zero
+//     (hardware range check) and need no clamping or clearing.  A tile has
+//     at least 3 K steps (short K is padded with such zero chunks), so the
+//     load streams never run more than one tile ahead.
+//   * Everything a tile needs from the kernel arguments (buffer resources of
+//     the next tile, its scales and bias) is fetched in the tile prologue,
+//     outside the K loop, which thus holds no scalar-memory load: the LDS
+//     waits the compiler places inside it count exactly.
 //   * One s_barrier per step, two MFMAs into the last sub-step: by then every
 //     fragment of the stage is in registers; the next stage's first fragments
 //     are read under the remaining MFMAs.
@@ -39,8 +43,8 @@
 //   * The MFMA takes Q_x as its first operand: for each accumulator register
 //     the 32 lanes of a half-wave hold 32 consecutive columns of one output
 //     row, so every 4-byte store instruction writes whole 128-byte lines.
-//   * s_x, s_w and b of a tile reach LDS by direct-to-LDS loads two tiles
-//     ahead, in a ring of three buffers.
+//   * s_x, s_w and b of a tile reach LDS by direct-to-LDS loads in the tile's
+//     prologue, in a ring of two buffers.
 //   * Loads and stores share one in-order counter (vmcnt).  Every wait names
 //     exactly the number of instructions issued after the awaited loads (this
 //     step's stores and the Q_w loads of two steps ahead).
@@ -48,6 +52,7 @@
 //     8 XCDs round robin) work on neighbouring tile rows and columns, which
 //     they then share in that XCD's L2.
 #include <mutex>
+#include <type_traits>
 #include <utility>
 
 #include "common.h"
@@ -67,6 +72,7 @@ constexpr int kBN = 192;       // tile columns
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kNumXcd = 8;
 constexpr int kGroupM = 4;
+constexpr int kMinSteps = 3;   // K steps per tile at least (see the header comment)
 constexpr int kVmMax = 63;     // largest vmcnt a wait can name
 // Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format).
 constexpr int kBufferWord3 = 0x00020000;
@@ -86,16 +92,15 @@ struct Cfg {
   static constexpr int WN = BN / 2;                       // wave tile columns
   static constexpr int FM = 4, FN = WN / 32;              // 32x32 blocks per wave
   static constexpr int NMF = FM * FN;                     // MFMAs per sub-step
-  static constexpr int NFR = FM + FN;                     // fragment reads per sub-step
   static constexpr int PR = (kBM + 2 * BN + 255) / 256;   // parameter loads per wave and tile
   static constexpr int PARB = PR * 256 * 4;               // bytes per parameter buffer
   static constexpr int PAR0 = WOFF + 3 * WSTAGE;          // LDS offset of the parameter ring
-  static constexpr int LDS = PAR0 + 3 * PARB;
+  static constexpr int LDS = PAR0 + 2 * PARB;
   static constexpr int NG = 32;                           // store groups per tile
   static constexpr int NV = 2 * FN;                       // values (stores) per group
+  static constexpr int NSS = NG / 2;                      // K steps that carry stores
   static_assert(kBM % 32 == 0 && BN % 32 == 0, "pieces must split over 4 waves");
-  static_assert(FN >= 2 && NFR + 2 <= NMF && XT + 2 <= NMF && XPW - XT <= NMF && WPW <= 2 * NMF,
-                "interleave slots");
+  static_assert(FN >= 2 && XT + 2 <= NMF && XPW - XT <= NMF && WPW <= 2 * NMF, "interleave slots");
   static_assert(NMF >= 2 * NV, "one store per odd slot");
   static_assert(LDS <= 160 * 1024, "LDS");
   static_assert(FM * FN * 16 == NG * NV, "store groups cover the tile");
@@ -165,24 +170,10 @@ CR_DEVICE void barrier() {
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14].
 template <int N>
 CR_DEVICE void waitvm_c() {
+  static_assert(N >= 0 && N <= kVmMax, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 CR_DEVICE void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-// Wait until at most n of this wave's memory instructions are in flight,
-// where n is L plus whole store groups of NV: exact for up to two groups,
-// stricter otherwise.
-template <int L, int NV>
-CR_DEVICE void wait_younger(int n) {
-  if (n >= L + 2 * NV)
-    waitvm_c<L + 2 * NV>();
-  else if (n >= L + NV)
-    waitvm_c<L + NV>();
-  else if (n >= L)
-    waitvm_c<L>();
-  else
-    waitvm_c<0>();
-}
 
 // Slot (MFMA index in [lo, n_slots)) of the i-th of n loads spread evenly
 // over a sub-step; -1 for no load at that slot.
@@ -200,22 +191,22 @@ CR_DEVICE __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
 template <int BN, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p) {
   using C = Cfg<BN>;
-  constexpr int FM = C::FM, FN = C::FN, NV = C::NV, NG = C::NG;
+  constexpr int FM = C::FM, FN = C::FN, NV = C::NV, NG = C::NG, NSS = C::NSS;
   __shared__ __attribute__((aligned(1024))) int8_t smem[C::LDS];
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  // wave, M and K are re-read through an empty asm statement at the top of
+  // every step and tile prologue (see reload_uniforms): values derived from
+  // them are then recomputed where they are used instead of being hoisted
+  // into the kernel prologue, where they would stay live (and spill) for the
+  // whole kernel.
+  int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = gridDim.x;
   const int slot = round_slot(blockIdx.x, G);
   const int ntiles = (p.total_tiles - slot + G - 1) / G;  // >= 1: grid <= tiles
-  const int nk = p.nk;
-  const int M = p.M, K = p.K;
-
-  // Memory instructions (loads and counted stores) this wave has issued.
-  // Edge-tile stores are not counted: a count that is too low only makes a
-  // wait stricter.
-  int issued = 0;
+  const int nk = p.nk;                                    // >= kMinSteps
+  int M = p.M, K = p.K;
+  auto reload_uniforms = [&]() { asm volatile("" : "+s"(wave), "+s"(M), "+s"(K)); };
 
   // ------------------------------------------------------------ loading
   // Piece q = wave + 4i of a stage holds its rows 8q .. 8q+7.  Lane l fills
@@ -224,35 +215,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
   // q & 1 = wave & 1 for every piece of a wave.  The two operands are loaded
   // as independent streams (Q_w runs one step further ahead); past the last
   // tile a stream repeats that tile into stages nobody reads any more.
-  const int ld_chunk = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
-  const int ld_off = (lane >> 3) * K + ld_chunk * 16;  // < 8 * K <= 2^21
+  auto ld_chunk = [&]() { return (lane & 7) ^ (lane >> 3) ^ (wave & 1); };
+  auto ld_off = [&]() { return (lane >> 3) * K + ld_chunk() * 16; };  // < 8 * K <= 2^21
   struct Stream {
-    __amdgpu_buffer_rsrc_t rs;
-    int it, ks, stage;
+    __amdgpu_buffer_rsrc_t rs, next;  // this tile's rows; the next tile's (set by its prologue)
+    int ks, stage;
     unsigned voff;  // this lane's offset in the current step, out of range past K
   };
-  Stream xs{buffer_rsrc(p.qx, 0), 0, 0, 0, kOutOfRange};
-  Stream ws{buffer_rsrc(p.qx, 0), 0, 0, 0, kOutOfRange};
-  // Before the first piece of a step: the tile's buffer resource when the
-  // stream enters a new tile, and the lane offset of the step.
+  auto x_rsrc = [&](int t_it) {
+    const TileInfo ti = tile_info<BN>(p, slot + t_it * G);
+    const int rows = M - ti.m0 < kBM ? M - ti.m0 : kBM;
+    return buffer_rsrc(p.qx + (int64_t)ti.m0 * K, rows * K);
+  };
+  auto w_rsrc = [&](int t_it) {
+    const TileInfo ti = tile_info<BN>(p, slot + t_it * G);
+    const Seg& sg = p.seg[ti.s];
+    const int rows = sg.n - ti.n0 < BN ? sg.n - ti.n0 : BN;
+    return buffer_rsrc(sg.qw + (int64_t)ti.n0 * K, rows * K);
+  };
+  Stream xs{x_rsrc(0), x_rsrc(0), 0, 0, kOutOfRange};
+  Stream ws{w_rsrc(0), w_rsrc(0), 0, 0, kOutOfRange};
   auto begin_x = [&]() {
-    if (xs.ks == 0) {
-      const TileInfo ti = tile_info<BN>(p, slot + (xs.it < ntiles ? xs.it : ntiles - 1) * G);
-      const int rows = M - ti.m0 < kBM ? M - ti.m0 : kBM;
-      xs.rs = buffer_rsrc(p.qx + (int64_t)ti.m0 * K, rows * K);
-    }
     const int k0 = xs.ks * C::BK;
-    xs.voff = (k0 + ld_chunk * 16 < K) ? unsigned(ld_off + k0) : kOutOfRange;
+    xs.voff = (k0 + ld_chunk() * 16 < K) ? unsigned(ld_off() + k0) : kOutOfRange;
   };
   auto begin_w = [&]() {
-    if (ws.ks == 0) {
-      const TileInfo ti = tile_info<BN>(p, slot + (ws.it < ntiles ? ws.it : ntiles - 1) * G);
-      const Seg& sg = p.seg[ti.s];
-      const int rows = sg.n - ti.n0 < BN ? sg.n - ti.n0 : BN;
-      ws.rs = buffer_rsrc(sg.qw + (int64_t)ti.n0 * K, rows * K);
-    }
     const int k0 = ws.ks * C::BK;
-    ws.voff = (k0 + ld_chunk * 16 < K) ? unsigned(ld_off + k0) : kOutOfRange;
+    ws.voff = (k0 + ld_chunk() * 16 < K) ? unsigned(ld_off() + k0) : kOutOfRange;
   };
   auto piece_x = [&](int i) {
     int8_t* dst = smem + xs.stage * C::XSTAGE + (wave + 4 * i) * 1024;
@@ -267,29 +256,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, off, 0, 0, 0);
   };
   auto end_x = [&]() {
-    issued += C::XPW;
     xs.stage ^= 1;
     if (++xs.ks == nk) {
       xs.ks = 0;
-      ++xs.it;
+      xs.rs = xs.next;
     }
   };
   auto end_w = [&]() {
-    issued += C::WPW;
     ws.stage = ws.stage == 2 ? 0 : ws.stage + 1;
     if (++ws.ks == nk) {
       ws.ks = 0;
-      ++ws.it;
+      ws.rs = ws.next;
     }
   };
-  // s_x | s_w | b of tile t_it into parameter buffer t_it % 3.  Float f of a
+  // s_x | s_w | b of tile t_it into parameter buffer t_it % 2.  Float f of a
   // buffer is loaded by wave (f / 64) % 4, lane f % 64 (padding loads s_x[0]).
   auto issue_params = [&](int t_it) {
     const TileInfo ti = tile_info<BN>(p, slot + t_it * G);
     const float* sw = p.seg[ti.s].sw;
     const float* bias = p.seg[ti.s].bias;
     const int n_lim = p.seg[ti.s].n - 1;
-    int8_t* par = smem + C::PAR0 + (t_it % 3) * C::PARB;
+    int8_t* par = smem + C::PAR0 + (t_it & 1) * C::PARB;
 #pragma unroll
     for (int rd = 0; rd < C::PR; ++rd) {
       const int f0 = rd * 256 + wave * 64;
@@ -306,7 +293,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
       }
       __builtin_amdgcn_global_load_lds(src, (lds_void*)(par + f0 * 4), 4, 0, 0);
     }
-    issued += C::PR;
   };
 
   // ----------------------------------------------------------- fragments
@@ -325,10 +311,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
   // end of a sub-step, alternate between two sets.
   v4i xf[FM], wf[2][FN];
   auto read_x = [&](const int8_t* xstage, int i, int kk) {
-    xf[i] = *reinterpret_cast<const v4i*>(xstage + fbase[kk] + (wm * 128 + i * 32) * 128);
+    xf[i] = *reinterpret_cast<const v4i*>(xstage + fbase[kk] + ((wave >> 1) * 128 + i * 32) * 128);
   };
   auto read_w = [&](const int8_t* wstage, int set, int j, int kk) {
-    wf[set][j] = *reinterpret_cast<const v4i*>(wstage + fbase[kk] + (wn * C::WN + j * 32) * 128);
+    wf[set][j] = *reinterpret_cast<const v4i*>(wstage + fbase[kk] + ((wave & 1) * C::WN + j * 32) * 128);
   };
   // The fragment reads that follow MFMA idx of a sub-step, for slice kk of
   // the given stages (the next sub-step's slice).
@@ -349,9 +335,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
   // 128-byte segment of two output rows.
   v32i pend[NV];
   int pd_valid = 0, pd_interior = 0, pd_n = 0, pd_par = C::PAR0;
-  int pd_next = 0;            // next group to store
-  int pd_due = 0, pd_rem = 0;  // groups due so far: floor(steps * NG / nk)
   int pd_row0 = 0, pd_col0 = 0;
+  int pd_sxo = 0;              // LDS offset of this lane's s_x for group 0
   int pd_m0w = 0, pd_n0w = 0;  // uniform parts: m0 + wm*128, n0 + wn*BN/2
   int pd_fast = 0;             // interior tile with a row stride that fits the fast path
   unsigned pd_voff = 0;        // lane part of a fast-path store address, in bytes
@@ -365,66 +350,53 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
     return pd_row0 + (q >> 3) * 32 + 8 * ((q >> 1) & 3) + 2 * (q & 1);
   };
   auto read_group_sx = [&](int q) -> f32x2 {
-    return *reinterpret_cast<const f32x2*>(smem + pd_par + (group_row(q) - pd_row0 + wm * 128 +
+    return *reinterpret_cast<const f32x2*>(smem + pd_par + (group_row(q) - pd_row0 + (wave >> 1) * 128 +
                                                                4 * (lane >> 5)) * 4);
   };
-  // Value e of group q: convert, scale, store (masked on edge tiles).
+  auto scaled = [&](int raw, float sx, int j) -> float {
+    if (MODE == kModeI32) return __int_as_float(raw);
+    float v = __builtin_fmaf((float)raw * sx, pd_sw[j], pd_b[j]);
+    if (MODE == kModeGelu) v = gelu_erf(v);
+    return v;
+  };
+  // Value e of group q, masked to the matrix (any tile).
   auto store_value = [&](int q, int e, f32x2 sx, float* yrow, int m) {
     const int j = e >> 1, rr = e & 1;
-    const int raw = pend[e][q];
-    float v;
-    if (MODE == kModeI32) {
-      v = __int_as_float(raw);
-    } else {
-      v = __builtin_fmaf((float)raw * sx[rr], pd_sw[j], pd_b[j]);
-      if (MODE == kModeGelu) v = gelu_erf(v);
-    }
+    const float v = scaled(pend[e][q], sx[rr], j);
     float* yp = yrow + rr * pd_ldy + j * 32;
-    if (pd_interior) {
-      *yp = v;
-    } else if (m + rr < M && pd_col0 + j * 32 < pd_n) {
-      *yp = v;
-    }
+    if (m + rr < M && pd_col0 + j * 32 < pd_n) *yp = v;
   };
   auto store_group = [&](int q, f32x2 sx) {
     const int m = group_row(q);
     float* yrow = pd_y + (int64_t)m * pd_ldy + pd_col0;
 #pragma unroll
     for (int e = 0; e < NV; ++e) store_value(q, e, sx, yrow, m);
-    if (pd_interior) issued += NV;
   };
-  // On interior tiles up to two groups per K step are stored one value per
-  // odd MFMA slot of sub-steps 1 and 2 (group 0, group 1), unmasked; the
-  // address is a uniform row base plus this lane's fixed 32-bit offset
-  // (4*(lane/32) rows and lane%32 columns), and the s_x of both groups are
-  // read before the preceding barrier.  Edge tiles drain through
-  // store_group at their last step.
-  f32x2 gsx[2] = {{0.f, 0.f}, {0.f, 0.f}};
-  char* gbase[2] = {nullptr, nullptr};  // row pd_m0w + row_u(group), column pd_n0w
-  int n_grp = 0;  // groups stored during this step's sub-steps 1 and 2
-  auto group_base = [&](int q) {
-    const int row = pd_m0w + (q >> 3) * 32 + 8 * ((q >> 1) & 3) + 2 * (q & 1);
-    return reinterpret_cast<char*>(pd_y) + ((int64_t)row * pd_ldy + pd_n0w) * 4;
+  // Fast path (interior tiles): the address is a uniform row base plus this
+  // lane's fixed 32-bit offset (4*(lane/32) rows and lane%32 columns).
+  auto group_rel = [&](int q) {  // row of group q relative to m0 + wm*128
+    return (q >> 3) * 32 + 8 * ((q >> 1) & 3) + 2 * (q & 1);
   };
+  auto group_base_from = [&](int m0w, int q) {
+    return reinterpret_cast<char*>(pd_y) + ((int64_t)(m0w + group_rel(q)) * pd_ldy + pd_n0w) * 4;
+  };
+  auto group_base = [&](int q) { return group_base_from(pd_m0w, q); };
   auto store_fast = [&](int q, char* base, f32x2 sx, int e) {
     const int j = e >> 1, rr = e & 1;
-    const int raw = pend[e][q];
-    float v;
-    if (MODE == kModeI32) {
-      v = __int_as_float(raw);
-    } else {
-      v = __builtin_fmaf((float)raw * sx[rr], pd_sw[j], pd_b[j]);
-      if (MODE == kModeGelu) v = gelu_erf(v);
-    }
+    const float v = scaled(pend[e][q], sx[rr], j);
     char* row = base + rr * pd_ldy * 4;
     *reinterpret_cast<float*>(row + pd_voff + j * 128) = v;
   };
+  auto store_group_fast = [&](int q) {
+    const f32x2 sx = read_group_sx(q);
+    char* base = group_base(q);
+#pragma unroll
+    for (int e = 0; e < NV; ++e) store_fast(q, base, sx, e);
+  };
 
   // ------------------------------------------------------------ prologue
-  // Parameters of the first two tiles, Q_x of step 0, Q_w of steps 0 and 1;
-  // after the barrier the first Q_x pieces of step 1.
-  issue_params(0);
-  if (ntiles > 1) issue_params(1);
+  // Q_x of step 0, Q_w of steps 0 and 1; after the barrier the first Q_x
+  // pieces of step 1.
   begin_x();
 #pragma unroll
   for (int i = 0; i < C::XPW; ++i) piece_x(i);
@@ -447,24 +419,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
 #pragma unroll
   for (int i = 0; i < C::XT; ++i) piece_x(i);
 
-  int cur_x = 0, cur_w = 0, it = 0;  // stages of the step being computed
+  int cur_x = 0, cur_w = 0;  // stages of the step being computed
 
   // One K step into acc; the first step of a tile starts from zero.  Step g
   // computes from Q_x stage g%2 and Q_w stage g%3; during it the rest of Q_x
-  // of step g+1 and all of Q_w of step g+2 are requested.
-  auto step = [&](int ks, auto first) __attribute__((always_inline)) {
+  // of step g+1 and all of Q_w of step g+2 are requested.  SG >= 0: the step
+  // also stores groups 2*SG and 2*SG+1 of the pending tile (fast path).
+  auto step = [&](auto first_t, auto store_t, int sg) __attribute__((always_inline)) {
+    constexpr bool FIRST = decltype(first_t)::value;
+    constexpr bool STORE = decltype(store_t)::value;
+    constexpr int NST = STORE ? 2 * NV : 0;  // stores issued by this step
+    reload_uniforms();
     const int8_t* cx = smem + cur_x * C::XSTAGE;
     const int8_t* cw = smem + C::WOFF + cur_w * C::WSTAGE;
     const int nxt_x = cur_x ^ 1, nxt_w = cur_w == 2 ? 0 : cur_w + 1;
     const int8_t* nx = smem + nxt_x * C::XSTAGE;
     const int8_t* nw = smem + C::WOFF + nxt_w * C::WSTAGE;
+    f32x2 gsx[2] = {{0.f, 0.f}, {0.f, 0.f}};
+    char* gbase[2] = {nullptr, nullptr};
+    if constexpr (STORE) {
+      gsx[0] = *reinterpret_cast<const f32x2*>(smem + pd_sxo + group_rel(2 * sg) * 4);
+      gsx[1] = *reinterpret_cast<const f32x2*>(smem + pd_sxo + group_rel(2 * sg + 1) * 4);
+      gbase[0] = group_base(2 * sg);
+      gbase[1] = group_base(2 * sg + 1);
+    }
 
     // Sub-step 0: fragments of sub-step 1, the remaining Q_x of step g+1.
 #pragma unroll
     for (int idx = 0; idx < C::NMF; ++idx) {
       const int i = idx / FN, j = idx % FN;
-      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-          xf[i], wf[0][j], decltype(first)::value ? v16i{} : acc[i][j], 0, 0, 0);
+      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf[i], wf[0][j], FIRST ? v16i{} : acc[i][j],
+                                                        0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       reads_after(idx, cx, cw, 1);
       {
@@ -474,24 +459,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
       __builtin_amdgcn_sched_barrier(0);
     }
     end_x();
-    const int a_x = issued;  // after this: stores, then Q_w loads
-
-    // Groups of the pending tile due by the end of this step.
-    n_grp = 0;
-    if (pd_valid) {
-      pd_rem += NG;
-      while (pd_rem >= nk) {
-        pd_rem -= nk;
-        ++pd_due;
-      }
-      n_grp = !pd_fast ? 0 : (pd_due - pd_next < 2 ? pd_due - pd_next : 2);
-      gbase[0] = group_base(pd_next);
-      gbase[1] = group_base(pd_next + 1);
-    }
     begin_w();
     __builtin_amdgcn_sched_barrier(0);
 
-    // Sub-steps 1 and 2: fragments, Q_w of step g+2.
+    // Sub-steps 1 and 2: fragments, Q_w of step g+2, the step's stores.
 #pragma unroll
     for (int kk = 1; kk < 3; ++kk) {
 #pragma unroll
@@ -501,9 +472,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
             __builtin_amdgcn_mfma_i32_32x32x32_i8(xf[i], wf[kk & 1][j], acc[i][j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         reads_after(idx, cx, cw, kk + 1);
-        // Group kk-1 of this step, one value per odd slot.
-        if ((idx & 1) && idx / 2 < NV && kk - 1 < n_grp)
-          store_fast(pd_next + kk - 1, gbase[kk - 1], gsx[kk - 1], idx / 2);
+        if constexpr (STORE) {
+          if ((idx & 1) && idx / 2 < NV)
+            store_fast(2 * sg + kk - 1, gbase[kk - 1], gsx[kk - 1], idx / 2);
+        }
         {
           constexpr int half = C::WPW / 2;
           const int pc = kk == 1 ? spread_piece(idx, 0, C::NMF, half)
@@ -514,10 +486,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
       }
     }
     end_w();
-    issued += n_grp * NV;
-    pd_next += n_grp;
-    // More than two groups per step (short K): the rest here.
-    for (; pd_next < pd_due; ++pd_next) store_group(pd_next, read_group_sx(pd_next));
 
     // Sub-step 3: wait, barrier, fragments and first Q_x loads of the next
     // stage.
@@ -528,13 +496,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
     }
     // Q_x of step g+1 and (issued a step earlier) Q_w of step g+1 have
     // landed once only this step's stores and Q_w loads may be in flight.
-    wait_younger<C::WPW, NV>(issued - a_x);
-    // s_x of the next step's two groups, complete at the wait below.
-    gsx[0] = read_group_sx(pd_next < NG ? pd_next : NG - 1);
-    gsx[1] = read_group_sx(pd_next + 1 < NG ? pd_next + 1 : NG - 1);
+    waitvm_c<C::WPW + NST>();
     wait_lgkm0();
     barrier();  // the next stages are readable by all, this step's are free
-    if (ks == nk - 1 && it + 2 < ntiles) issue_params(it + 2);
     begin_x();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -556,13 +520,39 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
     cur_w = nxt_w;
   };
 
-  for (it = 0; it < ntiles; ++it) {
-    step(0, std::true_type{});
-    for (int ks = 1; ks < nk; ++ks) step(ks, std::false_type{});
+  for (int it = 0; it < ntiles; ++it) {
+    // Tile prologue: the next tile's operand rows (the load streams enter it
+    // during this tile's last steps) and this tile's scales and bias.
+    {
+      reload_uniforms();
+      const int t1 = it + 1 < ntiles ? it + 1 : ntiles - 1;
+      xs.next = x_rsrc(t1);
+      ws.next = w_rsrc(t1);
+      issue_params(it);
+      wait_lgkm0();  // no scalar load stays in flight into the K loop
+    }
+    if (pd_fast) {
+      // The pending interior tile is stored two groups per step.
+      const int ns = nk < NSS ? nk : NSS;
+      step(std::true_type{}, std::true_type{}, 0);
+      for (int ks = 1; ks < ns; ++ks) step(std::false_type{}, std::true_type{}, ks);
+      for (int ks = ns; ks < nk; ++ks) step(std::false_type{}, std::false_type{}, 0);
+      if (nk < NSS) {  // short K: the groups left over
+        for (int q = 2 * nk; q < NG; ++q) store_group_fast(q);
+        wait_lgkm0();
+        barrier();  // the pending tile's parameter buffer is refilled next
+      }
+    } else {
+      if (pd_valid) {  // an edge tile: masked stores, before this tile's steps
+        for (int q = 0; q < NG; ++q) store_group(q, read_group_sx(q));
+      }
+      step(std::true_type{}, std::false_type{}, 0);
+      for (int ks = 1; ks < nk; ++ks) step(std::false_type{}, std::false_type{}, 0);
+    }
 
     // The tile is complete and the previous one fully stored: move the
-    // accumulators into pend.  The tile's parameters were requested two
-    // tiles ago and have been waited for since.
+    // accumulators into pend.  The tile's parameters were requested in its
+    // prologue and have been waited for since.
 #pragma unroll
     for (int q = 0; q < NG; ++q)
 #pragma unroll
@@ -571,42 +561,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
     const TileInfo ti = tile_info<BN>(p, slot + it * G);
     const Seg& sg = p.seg[ti.s];
     pd_valid = 1;
-    pd_next = 0;
-    pd_due = 0;
-    pd_rem = 0;
-    pd_par = C::PAR0 + (it % 3) * C::PARB;
-    pd_row0 = ti.m0 + wm * 128 + 4 * (lane >> 5);
-    pd_col0 = ti.n0 + wn * C::WN + (lane & 31);
+    pd_par = C::PAR0 + (it & 1) * C::PARB;
+    pd_sxo = pd_par + ((wave >> 1) * 128 + 4 * (lane >> 5)) * 4;
+    pd_row0 = ti.m0 + (wave >> 1) * 128 + 4 * (lane >> 5);
+    pd_col0 = ti.n0 + (wave & 1) * C::WN + (lane & 31);
     pd_y = static_cast<float*>(sg.y);
     pd_ldy = sg.ldy;
     pd_n = sg.n;
     pd_interior = (ti.m0 + kBM <= M) && (ti.n0 + BN <= sg.n);
-    pd_m0w = ti.m0 + wm * 128;
-    pd_n0w = ti.n0 + wn * C::WN;
+    pd_m0w = ti.m0 + (wave >> 1) * 128;
+    pd_n0w = ti.n0 + (wave & 1) * C::WN;
     pd_fast = pd_interior && sg.ldy < (int64_t(1) << 26);
     pd_voff = unsigned((4 * (lane >> 5)) * (int)(pd_fast ? sg.ldy : 0) + (lane & 31)) * 4u;
-    gsx[0] = read_group_sx(0);
-    gsx[1] = read_group_sx(1);
     const float* par = reinterpret_cast<const float*>(smem + pd_par);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int nl = wn * C::WN + j * 32 + (lane & 31);
+      const int nl = (wave & 1) * C::WN + j * 32 + (lane & 31);
       pd_sw[j] = par[kBM + nl];
       pd_b[j] = sg.bias ? par[kBM + BN + nl] : 0.f;
     }
   }
   // The last tile.
   if (pd_fast) {
-    for (; pd_next < NG; ++pd_next) {
-      const f32x2 sx = read_group_sx(pd_next);
-      char* base = group_base(pd_next);
-#pragma unroll
-      for (int e = 0; e < NV; ++e) store_fast(pd_next, base, sx, e);
-    }
+    for (int q = 0; q < NG; ++q) store_group_fast(q);
   } else {
-    for (; pd_next < NG; ++pd_next) store_group(pd_next, read_group_sx(pd_next));
+    for (int q = 0; q < NG; ++q) store_group(q, read_group_sx(q));
   }
-  waitvm_c<0>();         // no load into LDS may still be in flight at exit
+  waitvm_c<0>();  // no load into LDS may still be in flight at exit
 }
 
 int device_cu_count() {
@@ -636,6 +617,7 @@ hipError_t launch_t(GemmParams p, hipStream_t stream) {
   p.tiles_n = tn;
   p.total_tiles = p.tiles_m * tn;
   p.nk = (p.K + Cfg<BN>::BK - 1) / Cfg<BN>::BK;
+  if (p.nk < kMinSteps) p.nk = kMinSteps;  // the extra steps read zeros
   if (p.total_tiles == 0) return hipSuccess;
   const int cus = device_cu_count();
   const int grid = p.total_tiles < cus ? p.total_tiles : cus;
