@@ -590,22 +590,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
   waitvm_c<0>();  // no load into LDS may still be in flight at exit
 }
 
-int device_cu_count() {
-  static std::mutex mu;
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  std::lock_guard<std::mutex> lock(mu);
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
-
 template <int BN, int MODE>
 hipError_t launch_t(GemmParams p, hipStream_t stream) {
   p.tiles_m = (p.M + kBM - 1) / kBM;
@@ -626,6 +610,22 @@ hipError_t launch_t(GemmParams p, hipStream_t stream) {
 }
 
 }  // namespace
+
+int device_cu_count() {
+  static std::mutex mu;
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   GemmParams p{};

@@ -6,6 +6,9 @@
 
 namespace convrot {
 
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
 // Launch shape of the activation pack for a row length k (k % 16 == 0).
 struct PackPlan {
   int threads;            // workgroup size, 64..1024

@@ -33,6 +33,8 @@
 // absmax is a wave reduction.  No LDS and no barriers: a workgroup is just
 // four independent rows, and every row of the matrix can be in flight at
 // once, which is what an HBM-bound pass needs.
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -434,6 +436,8 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const InT* __restrict__ 
     const float s = ldexpf(mx, -log4g) / 127.0f;
     if (lane == 0) scale[row] = s;
     const float s_un = ldexpf(s, log4g);  // x_un / s_un == x / s exactly
+    // A zero row (s_un == 0) has only zeros, and with r = 0 the quotient
+    // below is then 0 as well: no per-element test is needed.
     const float r = (s_un != 0.f) ? 1.0f / s_un : 0.f;
     int8_t* qr = q + (int64_t)row * k;
 #pragma unroll
@@ -441,7 +445,7 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const InT* __restrict__ 
       int qi[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        qi[e] = s_un != 0.f ? clamp127(round_half_away_small(div_by_recip(v[c][e], s_un, r))) : 0;
+        qi[e] = clamp127(round_half_away_small(div_by_recip(v[c][e], s_un, r)));
       uint4 o;
       o.x = pack4_perm(qi[0], qi[1], qi[2], qi[3]);
       o.y = pack4_perm(qi[4], qi[5], qi[6], qi[7]);
@@ -455,9 +459,9 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const InT* __restrict__ 
 // G = 64 and 256: the digits held by lane bits 0-3 are brought into registers
 // by a 16 x 16 transpose through LDS inside each group of 16 lanes, so every
 // butterfly stage is a register stage (two adds per element) and the lane
-// exchange is LDS traffic instead of VALU work.  The codes are then stored
-// one byte per lane from the transposed layout (16 consecutive bytes per
-// group of 16 lanes): no packing.  A row's maximum satisfies |x| <= max, so
+// exchange is LDS traffic instead of VALU work.  The codes return to the
+// natural layout by a byte transpose through the same LDS buffer and leave
+// as 16-byte stores.  A row's maximum satisfies |x| <= max, so
 // |x / s| <= 127 (1 + 2^-23) and the code needs no clamp.
 constexpr int kTStride = 272;  // floats per 16-lane group: 256 + 16 (bank offset)
 
@@ -520,28 +524,45 @@ __global__ __launch_bounds__(256) void pack_rows_lds_kernel(const InT* __restric
     const float s = ldexpf(mx, -log4g) / 127.0f;
     if (lane == 0) scale[row] = s;
     const float s_un = ldexpf(s, log4g);
-    const float r = (s_un != 0.f) ? 1.0f / s_un : 0.f;
-    int8_t* qr = q + (int64_t)row * k + (16 * grp) * 16 + li;
+    const float r = (s_un != 0.f) ? 1.0f / s_un : 0.f;  // zero rows: codes 0 (see above)
+    // The codes go back to the natural layout through LDS as bytes (lane li
+    // writes byte li of each of its 16 chunks; lane li then reads chunk li
+    // whole), so each chunk leaves as one 16-byte store.  The float
+    // transpose above used the same buffer; a wave's LDS accesses run in
+    // order, so its reads are done before these writes land.
+    int8_t* tb = reinterpret_cast<int8_t*>(tw);
+    int8_t* qr = q + (int64_t)row * k + (16 * grp + li) * 16;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c)
+    for (int c = 0; c < CPL; ++c) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int code = s_un != 0.f ? round_half_away_small(div_by_recip(t[c][i], s_un, r)) : 0;
-        qr[(c * 64 + i) * 16] = (int8_t)code;
-      }
+      for (int i = 0; i < 16; ++i)
+        tb[i * 16 + li] = (int8_t)round_half_away_small(div_by_recip(t[c][i], s_un, r));
+      *reinterpret_cast<u32x4*>(qr + c * 64 * 16) = *reinterpret_cast<const u32x4*>(tb + li * 16);
+    }
   }
 }
 
 template <typename InT, int CPL>
 hipError_t launch_rows_t(const void* x, int64_t ldx, int m, int k, int log4g, int8_t* q,
                          float* scale, hipStream_t stream) {
-  // One row per wave up to 16 waves per CU (8 for rows of more than three
-  // chunks per lane, whose registers allow no more); beyond that each wave
+  // One row per wave up to as many waves as the chip holds at once (the
+  // kernel's register use decides how many fit per CU); beyond that each wave
   // walks several rows, loading the next while it transforms the current one.
-  const int cap = 256 * (CPL <= 3 ? 16 : 8);
-  const int waves = m < cap ? m : cap;
+  const bool lds = (log4g == 3 || log4g == 4);
+  const void* fn = lds ? reinterpret_cast<const void*>(&pack_rows_lds_kernel<InT, CPL>)
+                       : reinterpret_cast<const void*>(&pack_rows_kernel<InT, CPL>);
+  static std::atomic<int> blocks_per_cu[2];
+  int per_cu = blocks_per_cu[lds].load(std::memory_order_relaxed);
+  if (per_cu == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) != hipSuccess ||
+        per_cu <= 0)
+      per_cu = 2;
+    blocks_per_cu[lds].store(per_cu, std::memory_order_relaxed);
+  }
+  const int64_t cap = int64_t(device_cu_count()) * per_cu * 4;
+  const int waves = int(m < cap ? m : cap);
   const int grid = (waves + 3) / 4;
-  if (log4g == 3 || log4g == 4)
+  if (lds)
     hipLaunchKernelGGL((pack_rows_lds_kernel<InT, CPL>), dim3(grid), dim3(256), 0, stream,
                        static_cast<const InT*>(x), ldx, m, k, log4g, q, scale);
   else
