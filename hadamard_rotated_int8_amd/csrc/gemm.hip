@@ -63,7 +63,6 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
-typedef int v32i __attribute__((ext_vector_type(32)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -95,16 +94,22 @@ struct Cfg {
   static constexpr int PR = (kBM + 2 * BN + 255) / 256;   // parameter loads per wave and tile
   static constexpr int PARB = PR * 256 * 4;               // bytes per parameter buffer
   static constexpr int PAR0 = WOFF + 3 * WSTAGE;          // LDS offset of the parameter ring
-  static constexpr int LDS = PAR0 + 2 * PARB;
+  static constexpr int NPK = 3;                           // pending groups parked in LDS
+  static constexpr int PARK0 = PAR0 + 2 * PARB;           // LDS offset of the parking area
+  static constexpr int LDS = PARK0 + NPK * 6 * kThreads * 4;
   static constexpr int NG = 32;                           // store groups per tile
   static constexpr int NV = 2 * FN;                       // values (stores) per group
-  static constexpr int NSS = NG / 2;                      // K steps that carry stores
+  static constexpr int GPS = 4;                           // store groups per storing step
+  static constexpr int NSS = NG / GPS;                    // K steps that carry stores
+  static constexpr int GSUB = GPS / 2;                    // ... per storing sub-step (1 and 2)
+  static constexpr int ST = NMF / (GSUB * NV);            // MFMAs per store
   static_assert(kBM % 32 == 0 && BN % 32 == 0, "pieces must split over 4 waves");
   static_assert(FN >= 2 && XT + 2 <= NMF && XPW - XT <= NMF && WPW <= 2 * NMF, "interleave slots");
-  static_assert(NMF >= 2 * NV, "one store per odd slot");
+  static_assert(GPS % 2 == 0 && ST * GSUB * NV == NMF, "stores evenly spread over the middle sub-steps");
   static_assert(LDS <= 160 * 1024, "LDS");
   static_assert(FM * FN * 16 == NG * NV, "store groups cover the tile");
-  static_assert(WPW + 2 * NV <= kVmMax, "vmcnt range");
+  static_assert(WPW + GPS * NV <= kVmMax, "vmcnt range");
+  static_assert(NPK <= GPS, "parked groups are stored by the last storing step");
 };
 
 struct Seg {
@@ -181,6 +186,12 @@ constexpr int spread_piece(int idx, int lo, int n_slots, int n) {
   for (int i = 0; i < n; ++i)
     if (idx == lo + ((2 * i + 1) * (n_slots - lo)) / (2 * n)) return i;
   return -1;
+}
+
+// f(integral_constant<int, I>) for every I of the sequence, in order.
+template <int... I, typename F>
+CR_DEVICE void for_each_index(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, I>{}), ...);
 }
 
 CR_DEVICE __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
@@ -332,8 +343,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
   // column pd_col0 + (e / 2)*32, where pd_row0 = m0 + wm*128 + 4*(lane/32)
   // and pd_col0 = n0 + wn*BN/2 + lane%32.  Group q holds two rows of each of
   // the FN column blocks: NV store instructions, each writing a full
-  // 128-byte segment of two output rows.
-  v32i pend[NV];
+  // 128-byte segment of two output rows.  pend is only ever indexed with
+  // compile-time constants (the code that stores it is unrolled), so each
+  // value is a register of its own that is free again once stored.  The
+  // last NPK groups (stored last) wait in a per-thread LDS area instead: the
+  // register file, holding the running tile's accumulators as well, has no
+  // room left for them.
+  int pend[NG - C::NPK][NV];
+  auto park_slot = [&](int q, int e) -> int* {  // q >= NG - NPK
+    return reinterpret_cast<int*>(smem + C::PARK0) + ((q - (NG - C::NPK)) * NV + e) * kThreads +
+           threadIdx.x;
+  };
+  // Value e of pending group q (q a constant after unrolling).
+  auto pend_get = [&](int q, int e) -> int {
+    return q >= NG - C::NPK ? *park_slot(q, e) : pend[q < NG - C::NPK ? q : 0][e];
+  };
   int pd_valid = 0, pd_interior = 0, pd_n = 0, pd_par = C::PAR0;
   int pd_row0 = 0, pd_col0 = 0;
   int pd_sxo = 0;              // LDS offset of this lane's s_x for group 0
@@ -342,9 +366,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
   unsigned pd_voff = 0;        // lane part of a fast-path store address, in bytes
   float* pd_y = nullptr;
   int64_t pd_ldy = 0;
+  int pd_has_b = 0;             // the pending tile's weight has a bias
+  // s_w and b of the lane's columns for the paths that store outside the
+  // storing steps (edge tiles, short K, the last tile).
   float pd_sw[FN], pd_b[FN];
+  auto load_sw_b = [&]() {
 #pragma unroll
-  for (int j = 0; j < FN; ++j) pd_sw[j] = pd_b[j] = 0.f;
+    for (int j = 0; j < FN; ++j) {
+      const int nl = (wave & 1) * C::WN + j * 32 + (lane & 31);
+      pd_sw[j] = *reinterpret_cast<const float*>(smem + pd_par + (kBM + nl) * 4);
+      const float bv = *reinterpret_cast<const float*>(smem + pd_par + (kBM + BN + nl) * 4);
+      pd_b[j] = pd_has_b ? bv : 0.f;
+    }
+  };
 
   auto group_row = [&](int q) {  // output row of element e = 0 of group q
     return pd_row0 + (q >> 3) * 32 + 8 * ((q >> 1) & 3) + 2 * (q & 1);
@@ -353,16 +387,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
     return *reinterpret_cast<const f32x2*>(smem + pd_par + (group_row(q) - pd_row0 + (wave >> 1) * 128 +
                                                                4 * (lane >> 5)) * 4);
   };
-  auto scaled = [&](int raw, float sx, int j) -> float {
+  auto scaled_with = [&](int raw, float sx, float sw, float b) -> float {
     if (MODE == kModeI32) return __int_as_float(raw);
-    float v = __builtin_fmaf((float)raw * sx, pd_sw[j], pd_b[j]);
+    float v = __builtin_fmaf((float)raw * sx, sw, b);
     if (MODE == kModeGelu) v = gelu_erf(v);
     return v;
   };
+  auto scaled = [&](int raw, float sx, int j) -> float { return scaled_with(raw, sx, pd_sw[j], pd_b[j]); };
   // Value e of group q, masked to the matrix (any tile).
   auto store_value = [&](int q, int e, f32x2 sx, float* yrow, int m) {
     const int j = e >> 1, rr = e & 1;
-    const float v = scaled(pend[e][q], sx[rr], j);
+    const float v = scaled(pend_get(q, e), sx[rr], j);
     float* yp = yrow + rr * pd_ldy + j * 32;
     if (m + rr < M && pd_col0 + j * 32 < pd_n) *yp = v;
   };
@@ -381,12 +416,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
     return reinterpret_cast<char*>(pd_y) + ((int64_t)(m0w + group_rel(q)) * pd_ldy + pd_n0w) * 4;
   };
   auto group_base = [&](int q) { return group_base_from(pd_m0w, q); };
-  auto store_fast = [&](int q, char* base, f32x2 sx, int e) {
+  auto store_raw_with = [&](int raw, char* base, f32x2 sx, int e, float sw, float b) {
     const int j = e >> 1, rr = e & 1;
-    const float v = scaled(pend[e][q], sx[rr], j);
+    const float v = scaled_with(raw, sx[rr], sw, b);
     char* row = base + rr * pd_ldy * 4;
     *reinterpret_cast<float*>(row + pd_voff + j * 128) = v;
   };
+  auto store_raw = [&](int raw, char* base, f32x2 sx, int e) {
+    store_raw_with(raw, base, sx, e, pd_sw[e >> 1], pd_b[e >> 1]);
+  };
+  auto store_fast = [&](int q, char* base, f32x2 sx, int e) { store_raw(pend_get(q, e), base, sx, e); };
   auto store_group_fast = [&](int q) {
     const f32x2 sx = read_group_sx(q);
     char* base = group_base(q);
@@ -425,24 +464,58 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
   // computes from Q_x stage g%2 and Q_w stage g%3; during it the rest of Q_x
   // of step g+1 and all of Q_w of step g+2 are requested.  SG >= 0: the step
   // also stores groups 2*SG and 2*SG+1 of the pending tile (fast path).
-  auto step = [&](auto first_t, auto store_t, int sg) __attribute__((always_inline)) {
+  auto step = [&](auto first_t, auto ss_t) __attribute__((always_inline)) {
     constexpr bool FIRST = decltype(first_t)::value;
-    constexpr bool STORE = decltype(store_t)::value;
-    constexpr int NST = STORE ? 2 * NV : 0;  // stores issued by this step
+    constexpr int SS = decltype(ss_t)::value;   // storing step index, or -1
+    constexpr bool STORE = SS >= 0;
+    constexpr int GPS = C::GPS;
+    constexpr int NST = STORE ? GPS * NV : 0;  // stores issued by this step
     reload_uniforms();
     const int8_t* cx = smem + cur_x * C::XSTAGE;
     const int8_t* cw = smem + C::WOFF + cur_w * C::WSTAGE;
     const int nxt_x = cur_x ^ 1, nxt_w = cur_w == 2 ? 0 : cur_w + 1;
     const int8_t* nx = smem + nxt_x * C::XSTAGE;
     const int8_t* nw = smem + C::WOFF + nxt_w * C::WSTAGE;
-    f32x2 gsx[2] = {{0.f, 0.f}, {0.f, 0.f}};
-    char* gbase[2] = {nullptr, nullptr};
-    if constexpr (STORE) {
-      gsx[0] = *reinterpret_cast<const f32x2*>(smem + pd_sxo + group_rel(2 * sg) * 4);
-      gsx[1] = *reinterpret_cast<const f32x2*>(smem + pd_sxo + group_rel(2 * sg + 1) * 4);
-      gbase[0] = group_base(2 * sg);
-      gbase[1] = group_base(2 * sg + 1);
+    // s_x of the two groups a storing sub-step writes, read one sub-step
+    // ahead (only two are live at a time).
+    // s_w and b of the lane's columns, from the tile's parameter buffer
+    // (kept in LDS, not in registers, between the steps that store).
+    float gsw[FN], gb[FN];
+    if constexpr (STORE && MODE != kModeI32) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int nl = (wave & 1) * C::WN + j * 32 + (lane & 31);
+        gsw[j] = *reinterpret_cast<const float*>(smem + pd_par + (kBM + nl) * 4);
+        const float bv = *reinterpret_cast<const float*>(smem + pd_par + (kBM + BN + nl) * 4);
+        gb[j] = pd_has_b ? bv : 0.f;
+      }
     }
+    // The parked groups (the step's last NPK groups) of the last storing
+    // step, read from LDS one value per MFMA in the sub-step before the one
+    // that stores them.
+    int pk[C::NPK * NV];
+    constexpr int PK0 = GPS - C::NPK;  // first parked group within the step
+    auto read_parked = [&](int kk, int idx) {  // reads issued under MFMA idx of sub-step kk
+      if constexpr (SS == C::NSS - 1) {
+#pragma unroll
+        for (int v = 0; v < C::NPK * NV; ++v) {
+          const int g = PK0 + v / NV;            // group within the step
+          const int store_kk = 1 + g / C::GSUB;  // sub-step that stores it
+          const int slot = ((g % C::GSUB) * NV + v % NV) * C::ST;  // its store slot
+          if (kk == store_kk - 1 && idx == slot % C::NMF) pk[v] = *park_slot(NG - C::NPK + v / NV, v % NV);
+        }
+      }
+    };
+    f32x2 gsx[C::GSUB];
+    auto read_gsx = [&](int kk) {
+      if constexpr (STORE) {
+#pragma unroll
+        for (int g = 0; g < C::GSUB; ++g)
+          gsx[g] = *reinterpret_cast<const f32x2*>(
+              smem + pd_sxo + group_rel(GPS * SS + C::GSUB * (kk - 1) + g) * 4);
+      }
+    };
+    read_gsx(1);
 
     // Sub-step 0: fragments of sub-step 1, the remaining Q_x of step g+1.
 #pragma unroll
@@ -452,6 +525,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
                                                         0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       reads_after(idx, cx, cw, 1);
+      read_parked(0, idx);
       {
         const int pc = spread_piece(idx, 0, C::NMF, C::XPW - C::XT);
         if (pc >= 0) piece_x(C::XT + pc);
@@ -472,9 +546,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
             __builtin_amdgcn_mfma_i32_32x32x32_i8(xf[i], wf[kk & 1][j], acc[i][j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         reads_after(idx, cx, cw, kk + 1);
-        if constexpr (STORE) {
-          if ((idx & 1) && idx / 2 < NV)
-            store_fast(2 * sg + kk - 1, gbase[kk - 1], gsx[kk - 1], idx / 2);
+        if constexpr (STORE) {  // one store per ST MFMAs (constants after unrolling)
+          if (idx % C::ST == C::ST - 1) {
+            const int sn = idx / C::ST;
+            const int g = C::GSUB * (kk - 1) + sn / NV, e = sn % NV;
+            const int q = GPS * SS + g;
+            const int raw = q >= NG - C::NPK ? pk[(q - (NG - C::NPK)) * NV + e]
+                                             : pend[q < NG - C::NPK ? q : 0][e];
+            store_raw_with(raw, group_base(q), gsx[sn / NV], e, gsw[e >> 1], gb[e >> 1]);
+          }
+          if (kk == 1 && idx == C::NMF - 1) read_gsx(2);
+          read_parked(kk, idx);
         }
         {
           constexpr int half = C::WPW / 2;
@@ -532,22 +614,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
       wait_lgkm0();  // no scalar load stays in flight into the K loop
     }
     if (pd_fast) {
-      // The pending interior tile is stored two groups per step.
-      const int ns = nk < NSS ? nk : NSS;
-      step(std::true_type{}, std::true_type{}, 0);
-      for (int ks = 1; ks < ns; ++ks) step(std::false_type{}, std::true_type{}, ks);
-      for (int ks = ns; ks < nk; ++ks) step(std::false_type{}, std::false_type{}, 0);
+      // The pending interior tile is stored GPS groups per step over the
+      // tile's first NSS steps (unrolled: constant register indices).
+      for_each_index(std::make_integer_sequence<int, NSS>{}, [&](auto ss) {
+        constexpr int S = decltype(ss)::value;
+        if (S < nk) step(std::integral_constant<bool, S == 0>{}, ss);
+      });
+      for (int ks = NSS; ks < nk; ++ks) step(std::false_type{}, std::integral_constant<int, -1>{});
       if (nk < NSS) {  // short K: the groups left over
-        for (int q = 2 * nk; q < NG; ++q) store_group_fast(q);
+        load_sw_b();
+        for_each_index(std::make_integer_sequence<int, NG>{}, [&](auto qc) {
+          constexpr int Q = decltype(qc)::value;
+          if (Q >= C::GPS * nk) store_group_fast(Q);
+        });
         wait_lgkm0();
         barrier();  // the pending tile's parameter buffer is refilled next
       }
     } else {
       if (pd_valid) {  // an edge tile: masked stores, before this tile's steps
-        for (int q = 0; q < NG; ++q) store_group(q, read_group_sx(q));
+        load_sw_b();
+        for_each_index(std::make_integer_sequence<int, NG>{}, [&](auto qc) {
+          constexpr int Q = decltype(qc)::value;
+          store_group(Q, read_group_sx(Q));
+        });
       }
-      step(std::true_type{}, std::false_type{}, 0);
-      for (int ks = 1; ks < nk; ++ks) step(std::false_type{}, std::false_type{}, 0);
+      step(std::true_type{}, std::integral_constant<int, -1>{});
+      for (int ks = 1; ks < nk; ++ks) step(std::false_type{}, std::integral_constant<int, -1>{});
     }
 
     // The tile is complete and the previous one fully stored: move the
@@ -557,7 +649,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
     for (int q = 0; q < NG; ++q)
 #pragma unroll
       for (int e = 0; e < NV; ++e)
-        pend[e][q] = acc[q >> 3][e >> 1][4 * ((q >> 1) & 3) + 2 * (q & 1) + (e & 1)];
+      {
+        const int v = acc[q >> 3][e >> 1][4 * ((q >> 1) & 3) + 2 * (q & 1) + (e & 1)];
+        if (q >= NG - C::NPK)
+          *park_slot(q, e) = v;
+        else
+          pend[q < NG - C::NPK ? q : 0][e] = v;
+      }
     const TileInfo ti = tile_info<BN>(p, slot + it * G);
     const Seg& sg = p.seg[ti.s];
     pd_valid = 1;
@@ -573,19 +671,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
     pd_n0w = ti.n0 + (wave & 1) * C::WN;
     pd_fast = pd_interior && sg.ldy < (int64_t(1) << 26);
     pd_voff = unsigned((4 * (lane >> 5)) * (int)(pd_fast ? sg.ldy : 0) + (lane & 31)) * 4u;
-    const float* par = reinterpret_cast<const float*>(smem + pd_par);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int nl = (wave & 1) * C::WN + j * 32 + (lane & 31);
-      pd_sw[j] = par[kBM + nl];
-      pd_b[j] = sg.bias ? par[kBM + BN + nl] : 0.f;
-    }
+    pd_has_b = sg.bias != nullptr;
   }
   // The last tile.
+  load_sw_b();
   if (pd_fast) {
-    for (int q = 0; q < NG; ++q) store_group_fast(q);
+    for_each_index(std::make_integer_sequence<int, NG>{},
+                   [&](auto qc) { store_group_fast(decltype(qc)::value); });
   } else {
-    for (int q = 0; q < NG; ++q) store_group(q, read_group_sx(q));
+    for_each_index(std::make_integer_sequence<int, NG>{}, [&](auto qc) {
+      constexpr int Q = decltype(qc)::value;
+      store_group(Q, read_group_sx(Q));
+    });
   }
   waitvm_c<0>();  // no load into LDS may still be in flight at exit
 }
