@@ -18,6 +18,7 @@ timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +33,10 @@ if ROOT not in sys.path:
 PEAK_INT8_TOPS = 5000.0   # MI355X dense INT8 MFMA, 5.0 POP/s
 PEAK_HBM_GBPS = 8000.0    # MI355X HBM3E, 8 TB/s
 
+GEMM_SOURCE = os.path.join(ROOT, "hadamard_rotated_int8_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_qkv_4096x3072x9216_traffic.json")
+CALIBRATION_BYTES = 256 * 1024 * 1024  # the plain copy whose counters scale FETCH/WRITE_SIZE
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -42,7 +47,38 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device-to-device copy of CALIBRATION_BYTES "
+                         "(reads and writes that many bytes), for scaling HBM byte counters")
     return ap.parse_args()
+
+
+def gemm_traffic():
+    """HBM bytes per grouped Q/K/V GEMM launch from the committed counter
+    summary, or None when the GEMM source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(GEMM_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_source_sha256") != sha:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def calibrate_copy():
+    import torch
+
+    n = CALIBRATION_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": CALIBRATION_BYTES, "launches": 5}), flush=True)
 
 
 def cpu_baseline(inp, w, g, target_s):
@@ -88,6 +124,10 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     import torch
 
@@ -201,7 +241,7 @@ def main():
             "peak": PEAK_INT8_TOPS,
             "unit": "TFLOP/s",
             "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
-            "traffic": None,
+            "traffic": gemm_traffic(),
         },
     }
     if not args.no_cpu_baseline:
