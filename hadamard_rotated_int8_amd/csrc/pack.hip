@@ -465,23 +465,39 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const InT* __restrict__ 
 // |x / s| <= 127 (1 + 2^-23) and the code needs no clamp.
 constexpr int kTStride = 272;  // floats per 16-lane group: 256 + 16 (bank offset)
 
-template <typename InT, int CPL>
+// WPR waves share one row (rows longer than one wave holds): wave w of a
+// workgroup takes part w % WPR of row slot w / WPR, the parts' maxima meet in
+// LDS (one barrier per row).  All waves of a workgroup then walk the same
+// number of rows, so a slot past the last row only joins the barrier.
+template <typename InT, int CPL, int WPR>
 __global__ __launch_bounds__(256) void pack_rows_lds_kernel(const InT* __restrict__ x,
                                                             int64_t ldx, int m, int k,
                                                             int log4g, int8_t* __restrict__ q,
                                                             float* __restrict__ scale) {
+  static_assert(WPR == 1 || WPR == 2 || WPR == 4, "waves per row");
+  constexpr int RPB = 4 / WPR;  // rows per workgroup at a time
   __shared__ __attribute__((aligned(16))) float tbuf[4][4 * kTStride];
+  __shared__ float red[2][4];   // per-wave maxima, by row parity
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
+  const int part = wv % WPR;
   const int grp = lane >> 4, li = lane & 15;
-  const int nw = gridDim.x * 4;
-  int row = blockIdx.x * 4 + wv;
-  if (row >= m) return;  // the whole wave: no barriers below
+  const int nr = gridDim.x * RPB;
+  int row = blockIdx.x * RPB + wv / WPR;
+  if (WPR == 1 && row >= m) return;  // the whole wave: no barriers below
+  // This wave's part of a row: chunks part*CPL*64 .. (part+1)*CPL*64 - 1.
+  const int64_t col0 = int64_t(part) * CPL * 64 * 16;
   float* tw = &tbuf[wv][grp * kTStride];
   RawChunk<InT> raw[CPL];
+  if (row < m) {
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) raw[c].load(x + (int64_t)row * ldx + (int64_t)(c * 64 + lane) * 16);
-  for (; row < m; row += nw) {
+    for (int c = 0; c < CPL; ++c)
+      raw[c].load(x + (int64_t)row * ldx + col0 + (int64_t)(c * 64 + lane) * 16);
+  }
+  // One wave per row: the wave's own row decides; shared rows: the
+  // workgroup's first row, so that every wave meets every barrier.
+  for (int it = 0; WPR == 1 ? row < m : blockIdx.x * RPB + it * nr < m; ++it, row += nr) {
+    const bool live = row < m;
     // t[c][i] = element li of chunk c*64 + 16*grp + i, after the transpose
     float t[CPL][16];
 #pragma unroll
@@ -499,11 +515,11 @@ __global__ __launch_bounds__(256) void pack_rows_lds_kernel(const InT* __restric
 #pragma unroll
       for (int i = 0; i < 16; ++i) t[c][i] = tw[i * 16 + li];
     }
-    const int nrow = row + nw;
+    const int nrow = row + nr;
     if (nrow < m) {
 #pragma unroll
       for (int c = 0; c < CPL; ++c)
-        raw[c].load(x + (int64_t)nrow * ldx + (int64_t)(c * 64 + lane) * 16);
+        raw[c].load(x + (int64_t)nrow * ldx + col0 + (int64_t)(c * 64 + lane) * 16);
     }
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
@@ -521,8 +537,15 @@ __global__ __launch_bounds__(256) void pack_rows_lds_kernel(const InT* __restric
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(t[c][e]));
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    if constexpr (WPR > 1) {
+      if (lane == 0) red[it & 1][wv] = mx;
+      __syncthreads();  // red[it & 1] is rewritten two rows later, after another barrier
+#pragma unroll
+      for (int w2 = 0; w2 < WPR; ++w2) mx = fmaxf(mx, red[it & 1][(wv / WPR) * WPR + w2]);
+    }
+    if (!live) continue;
     const float s = ldexpf(mx, -log4g) / 127.0f;
-    if (lane == 0) scale[row] = s;
+    if (lane == 0 && part == 0) scale[row] = s;
     const float s_un = ldexpf(s, log4g);
     const float r = (s_un != 0.f) ? 1.0f / s_un : 0.f;  // zero rows: codes 0 (see above)
     // The codes go back to the natural layout through LDS as bytes (lane li
@@ -531,7 +554,7 @@ __global__ __launch_bounds__(256) void pack_rows_lds_kernel(const InT* __restric
     // transpose above used the same buffer; a wave's LDS accesses run in
     // order, so its reads are done before these writes land.
     int8_t* tb = reinterpret_cast<int8_t*>(tw);
-    int8_t* qr = q + (int64_t)row * k + (16 * grp + li) * 16;
+    int8_t* qr = q + (int64_t)row * k + col0 + (16 * grp + li) * 16;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
 #pragma unroll
@@ -542,14 +565,16 @@ __global__ __launch_bounds__(256) void pack_rows_lds_kernel(const InT* __restric
   }
 }
 
-template <typename InT, int CPL>
+template <typename InT, int CPL, int WPR>
 hipError_t launch_rows_t(const void* x, int64_t ldx, int m, int k, int log4g, int8_t* q,
                          float* scale, hipStream_t stream) {
-  // One row per wave up to as many waves as the chip holds at once (the
-  // kernel's register use decides how many fit per CU); beyond that each wave
-  // walks several rows, loading the next while it transforms the current one.
+  // One row per WPR waves, up to as many waves as the chip holds at once (the
+  // kernel's register use decides how many fit per CU); beyond that each
+  // wave walks several rows, loading the next while it transforms the
+  // current one.  Only G = 64 and 256 split a row over several waves.
   const bool lds = (log4g == 3 || log4g == 4);
-  const void* fn = lds ? reinterpret_cast<const void*>(&pack_rows_lds_kernel<InT, CPL>)
+  if (WPR > 1 && !lds) return hipErrorInvalidValue;
+  const void* fn = lds ? reinterpret_cast<const void*>(&pack_rows_lds_kernel<InT, CPL, WPR>)
                        : reinterpret_cast<const void*>(&pack_rows_kernel<InT, CPL>);
   static std::atomic<int> blocks_per_cu[2];
   int per_cu = blocks_per_cu[lds].load(std::memory_order_relaxed);
@@ -560,10 +585,11 @@ hipError_t launch_rows_t(const void* x, int64_t ldx, int m, int k, int log4g, in
     blocks_per_cu[lds].store(per_cu, std::memory_order_relaxed);
   }
   const int64_t cap = int64_t(device_cu_count()) * per_cu * 4;
-  const int waves = int(m < cap ? m : cap);
+  const int64_t want = int64_t(m) * WPR;
+  const int waves = int(want < cap ? want : cap);
   const int grid = (waves + 3) / 4;
   if (lds)
-    hipLaunchKernelGGL((pack_rows_lds_kernel<InT, CPL>), dim3(grid), dim3(256), 0, stream,
+    hipLaunchKernelGGL((pack_rows_lds_kernel<InT, CPL, WPR>), dim3(grid), dim3(256), 0, stream,
                        static_cast<const InT*>(x), ldx, m, k, log4g, q, scale);
   else
     hipLaunchKernelGGL((pack_rows_kernel<InT, CPL>), dim3(grid), dim3(256), 0, stream,
@@ -571,18 +597,36 @@ hipError_t launch_rows_t(const void* x, int64_t ldx, int m, int k, int log4g, in
   return hipGetLastError();
 }
 
+// Rows of k = n * 1024 features: one wave per row for n <= 8; for G = 64
+// and 256 also n = 10, 14 (two waves per row) and n = 12, 16, ..., 32 (four).
+bool rows_supported(int64_t k, int log4g) {
+  if (k % 1024 != 0) return false;
+  const int64_t n = k / 1024;
+  if (n >= 1 && n <= 8) return log4g <= 5;
+  if (log4g != 3 && log4g != 4) return false;
+  return n == 10 || n == 14 || (n % 4 == 0 && n <= 32);
+}
+
 template <typename InT>
 hipError_t launch_rows(const void* x, int64_t ldx, int m, int k, int log4g, int8_t* q,
                        float* scale, hipStream_t stream) {
   switch (k / 1024) {
-    case 1: return launch_rows_t<InT, 1>(x, ldx, m, k, log4g, q, scale, stream);
-    case 2: return launch_rows_t<InT, 2>(x, ldx, m, k, log4g, q, scale, stream);
-    case 3: return launch_rows_t<InT, 3>(x, ldx, m, k, log4g, q, scale, stream);
-    case 4: return launch_rows_t<InT, 4>(x, ldx, m, k, log4g, q, scale, stream);
-    case 5: return launch_rows_t<InT, 5>(x, ldx, m, k, log4g, q, scale, stream);
-    case 6: return launch_rows_t<InT, 6>(x, ldx, m, k, log4g, q, scale, stream);
-    case 7: return launch_rows_t<InT, 7>(x, ldx, m, k, log4g, q, scale, stream);
-    case 8: return launch_rows_t<InT, 8>(x, ldx, m, k, log4g, q, scale, stream);
+    case 1: return launch_rows_t<InT, 1, 1>(x, ldx, m, k, log4g, q, scale, stream);
+    case 2: return launch_rows_t<InT, 2, 1>(x, ldx, m, k, log4g, q, scale, stream);
+    case 3: return launch_rows_t<InT, 3, 1>(x, ldx, m, k, log4g, q, scale, stream);
+    case 4: return launch_rows_t<InT, 4, 1>(x, ldx, m, k, log4g, q, scale, stream);
+    case 5: return launch_rows_t<InT, 5, 1>(x, ldx, m, k, log4g, q, scale, stream);
+    case 6: return launch_rows_t<InT, 6, 1>(x, ldx, m, k, log4g, q, scale, stream);
+    case 7: return launch_rows_t<InT, 7, 1>(x, ldx, m, k, log4g, q, scale, stream);
+    case 8: return launch_rows_t<InT, 8, 1>(x, ldx, m, k, log4g, q, scale, stream);
+    case 10: return launch_rows_t<InT, 5, 2>(x, ldx, m, k, log4g, q, scale, stream);
+    case 14: return launch_rows_t<InT, 7, 2>(x, ldx, m, k, log4g, q, scale, stream);
+    case 12: return launch_rows_t<InT, 3, 4>(x, ldx, m, k, log4g, q, scale, stream);
+    case 16: return launch_rows_t<InT, 4, 4>(x, ldx, m, k, log4g, q, scale, stream);
+    case 20: return launch_rows_t<InT, 5, 4>(x, ldx, m, k, log4g, q, scale, stream);
+    case 24: return launch_rows_t<InT, 6, 4>(x, ldx, m, k, log4g, q, scale, stream);
+    case 28: return launch_rows_t<InT, 7, 4>(x, ldx, m, k, log4g, q, scale, stream);
+    case 32: return launch_rows_t<InT, 8, 4>(x, ldx, m, k, log4g, q, scale, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -625,7 +669,7 @@ PackPlan plan_pack(int64_t k) {
 hipError_t launch_pack(const void* x, bool bf16, int64_t ldx, int64_t m, int64_t k, int log4g,
                        int8_t* q, float* scale, hipStream_t stream) {
   const int mi = int(m), ki = int(k);
-  if (log4g <= 5 && k % 1024 == 0 && k / 1024 <= 8) {
+  if (rows_supported(k, log4g)) {
     return bf16 ? launch_rows<uint16_t>(x, ldx, mi, ki, log4g, q, scale, stream)
                 : launch_rows<float>(x, ldx, mi, ki, log4g, q, scale, stream);
   }

@@ -169,6 +169,31 @@ def test_pack_long_rows(k, g, dt):
     check_pack(host(p.q), host(p.scale), q_or, s_or, f"k={k} G={g}")
 
 
+@pytest.mark.parametrize("k,g,dt,m", [(10240, 256, "bf16", 7), (12288, 256, "f32", 13),
+                                       (12288, 64, "bf16", 1031), (14336, 64, "f32", 5),
+                                       (16384, 256, "bf16", 3), (20480, 64, "bf16", 2),
+                                       (24576, 256, "f32", 6), (28672, 256, "bf16", 1),
+                                       (32768, 256, "f32", 9)])
+def test_pack_rows_split_over_waves(k, g, dt, m):
+    """Rows of 10..32 K features shared by two or four waves (G = 64, 256),
+    with row counts that leave workgroup slots empty."""
+    rng = np.random.default_rng(k + m)
+    x32 = rng.standard_normal((m, k)).astype(np.float32)
+    x32[:, rng.choice(k, 7, replace=False)] *= 30
+    if m > 2:
+        x32[m // 2] = 0
+    if dt == "bf16":
+        xt = torch.from_numpy(x32).to(torch.bfloat16)
+        x64 = xt.to(torch.float64).numpy()
+    else:
+        xt = torch.from_numpy(x32)
+        x64 = x32.astype(np.float64)
+    _say(f"pack split rows k={k} G={g} {dt} m={m}")
+    p = cr.pack_activations(xt.cuda(), g)
+    q_or, s_or = orc.pack_activations(x64, g)
+    check_pack(host(p.q), host(p.scale), q_or, s_or, f"k={k} G={g} m={m}")
+
+
 def test_pack_strided_input_and_reuse_of_output():
     rng = np.random.default_rng(8)
     big = rng.standard_normal((40, 2048 + 64)).astype(np.float32)
