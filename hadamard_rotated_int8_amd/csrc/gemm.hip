@@ -43,6 +43,8 @@
 //   * The MFMA takes Q_x as its first operand: for each accumulator register
 //     the 32 lanes of a half-wave hold 32 consecutive columns of one output
 //     row, so every 4-byte store instruction writes whole 128-byte lines.
+//     Output stores are non-temporal: Y is written once and should not push
+//     the operand slices the other CUs of the XCD still read out of L2.
 //   * s_x, s_w and b of a tile reach LDS by direct-to-LDS loads in the tile's
 //     prologue, in a ring of two buffers.
 //   * Loads and stores share one in-order counter (vmcnt).  Every wait names
@@ -163,7 +165,27 @@ CR_DEVICE int round_slot(int b, int G) {
   return (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
 }
 
-CR_DEVICE float gelu_erf(float y) { return 0.5f * y * (1.0f + erff(y * 0.70710678118654752f)); }
+// erf(x) by Abramowitz & Stegun, Handbook of Mathematical Functions,
+// formula 7.1.26: for a >= 0, erf(a) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) e^{-a^2}
+// with t = 1 / (1 + p a), absolute error at most 1.5e-7; erf is odd.  About
+// a dozen VALU operations (hardware reciprocal and base-2 exponential)
+// instead of the device library's longer branch-and-select sequence, which
+// matters because the epilogue evaluates it for every output.
+CR_DEVICE float erf_as(float x) {
+  const float a = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, a, 1.0f));
+  float poly = __builtin_fmaf(t, 1.061405429f, -1.453152027f);
+  poly = __builtin_fmaf(t, poly, 1.421413741f);
+  poly = __builtin_fmaf(t, poly, -0.284496736f);
+  poly = __builtin_fmaf(t, poly, 0.254829592f);
+  poly *= t;
+  const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * a * a);  // e^{-a^2}
+  const float r = __builtin_fmaf(-poly, e, 1.0f);
+  return __builtin_copysignf(r, x);
+}
+
+// GELU, the erf form x * Phi(x) = x/2 (1 + erf(x / sqrt 2)).
+CR_DEVICE float gelu_erf(float y) { return 0.5f * y * (1.0f + erf_as(y * 0.70710678118654752f)); }
 
 CR_DEVICE void barrier() {
   // A bare s_barrier: the waits are issued explicitly, and the memory clobber
@@ -399,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
     const int j = e >> 1, rr = e & 1;
     const float v = scaled(pend_get(q, e), sx[rr], j);
     float* yp = yrow + rr * pd_ldy + j * 32;
-    if (m + rr < M && pd_col0 + j * 32 < pd_n) *yp = v;
+    if (m + rr < M && pd_col0 + j * 32 < pd_n) __builtin_nontemporal_store(v, yp);
   };
   auto store_group = [&](int q, f32x2 sx) {
     const int m = group_row(q);
@@ -420,7 +442,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
     const int j = e >> 1, rr = e & 1;
     const float v = scaled_with(raw, sx[rr], sw, b);
     char* row = base + rr * pd_ldy * 4;
-    *reinterpret_cast<float*>(row + pd_voff + j * 128) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<float*>(row + pd_voff + j * 128));
   };
   auto store_raw = [&](int raw, char* base, f32x2 sx, int e) {
     store_raw_with(raw, base, sx, e, pd_sw[e >> 1], pd_b[e >> 1]);
