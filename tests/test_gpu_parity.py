@@ -525,3 +525,32 @@ def test_full_size_sampled(name):
         assert np.array_equal(host(qw.q), qw_or) and np.array_equal(host(qw.scale), sw_or)
         y_or = orc.linear(qx_or, sx_or, qw_or, sw_or, b, act="gelu" if w.gelu_chain else None)
         check_y(yr, y_or, sx_or, sw_or, w.k, gelu=w.gelu_chain, what=f"{name}[{li}]")
+
+
+# ---------------------------------------------------------------------------
+# Checkpoint round trip: stored codes through the HIP path
+# ---------------------------------------------------------------------------
+
+def test_linear_from_checkpoint(tmp_path):
+    """A convrot safetensors file (oracle-quantised weights, ComfyUI [out, 1]
+    scales) loaded onto the device and used as stored, against the oracle."""
+    from hadamard_rotated_int8_amd import checkpoint as ck
+
+    inp = wl.generate(wl.QKV, m=192, n_limit=700)
+    g = 256
+    mods = {}
+    for name, wt, b in zip(("q", "k", "v"), inp["weights"], inp["biases"]):
+        q_or, s_or = orc.quantize_weights(wt, g)
+        mods[f"attn.{name}"] = (q_or, s_or, b, g)
+    path = str(tmp_path / "attn.safetensors")
+    ck.save_checkpoint(path, mods)
+    _say("linear from checkpoint")
+    loaded = ck.load_checkpoint(path, device="cuda")
+    ws = [ck.to_weights(loaded[f"attn.{n}"]) for n in ("q", "k", "v")]
+    p = cr.pack_activations(dev(inp["x"]), g)
+    ys = cr.linear_grouped(p, ws)
+    qx_or, sx_or = orc.pack_activations(inp["x64"], g)
+    for y, n in zip(ys, ("q", "k", "v")):
+        q_or, s_or, b, _ = mods[f"attn.{n}"]
+        y_or = orc.linear(qx_or, sx_or, q_or, s_or, b)
+        check_y(host(y), y_or, sx_or, s_or, wl.QKV.k, what=f"checkpoint {n}")
