@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="instead of the step line: one JSON line per workload and kernel "
+                         "(pack GB/s, linear TOPS, roofline fractions, oracle baseline on a row sample)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device-to-device copy of CALIBRATION_BYTES "
                          "(reads and writes that many bytes), for scaling HBM byte counters")
@@ -66,6 +69,127 @@ def gemm_traffic():
     if t.get("gemm_source_sha256") != sha:
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def _time_ms(fn, reps=20, flush=None):
+    """Average ms per call over back-to-back launches, or the median of single
+    launches each after a cache-flushing write when ``flush`` is given."""
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    if flush is None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+    ts = []
+    for _ in range(reps):
+        flush.fill_(1.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts))
+
+
+def all_configs(args):
+    """Every workload: the pack per group size and each linear, as JSON lines."""
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import hadamard_rotated_int8_amd as cr
+    import workloads as wl
+    from oracle import convrot_oracle as orc
+
+    cr.lib()
+    cores = len(os.sched_getaffinity(0))
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+
+    def emit(**kw):
+        print(json.dumps(kw), flush=True)
+
+    def oracle_tops(x64_rows, qws_or, g, n_total):
+        """The oracle (pack + linears) on a row sample, as TOPS on this host."""
+        with threadpool_limits(limits=cores):
+            t0 = time.perf_counter()
+            qx, sx = orc.pack_activations(x64_rows, g)
+            for q, sw in qws_or:
+                orc.linear(qx, sx, q, sw, None)
+            dt = time.perf_counter() - t0
+        return 2.0 * x64_rows.shape[0] * n_total * x64_rows.shape[1] / dt / 1e12
+
+    for w in wl.ORDER:
+        inp = wl.generate(w)
+        x = inp["x"].cuda()
+        m, k = w.m, w.k
+        xb = x.element_size()
+        for g in w.group_sizes:
+            qws = [cr.quantize_weights(torch.from_numpy(wt).cuda(), g, torch.from_numpy(b).cuda())
+                   for wt, b in zip(inp["weights"], inp["biases"])]
+            packed = cr.pack_activations(x, g)
+            pbytes = m * k * (xb + 1) + 4 * m
+            warm = _time_ms(lambda: cr.pack_activations(x, g, out=packed))
+            cold = _time_ms(lambda: cr.pack_activations(x, g, out=packed), reps=10, flush=flush)
+            emit(workload=w.name, kernel="pack", m=m, k=k, x_dtype=w.x_dtype, group_size=g,
+                 us_warm=round(warm * 1e3, 2), us_cold=round(cold * 1e3, 2),
+                 gbps_cold=round(pbytes / (cold * 1e-3) / 1e9, 1),
+                 hbm_frac_cold=round(pbytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4))
+            linears = list(zip(w.linears, qws))
+            if w.gelu_chain:
+                linears = linears[:1]
+            for spec, qw in linears:
+                gl = w.gelu_chain
+                y = torch.empty((m, spec.n), dtype=torch.float32, device="cuda")
+                t = _time_ms(lambda: cr.linear(packed, qw, out=y, gelu=gl))
+                tops = 2.0 * m * spec.n * k / (t * 1e-3) / 1e12
+                emit(workload=w.name, kernel="linear", linear=spec.name, m=m, n=spec.n, k=k,
+                     group_size=g, gelu=gl, us=round(t * 1e3, 2), tops=round(tops, 1),
+                     mfma_frac=round(tops / PEAK_INT8_TOPS, 4))
+                if w.gelu_chain:  # the down projection on this (float32) output
+                    dspec, dqw = w.linears[1], qws[1]
+                    hp = cr.pack_activations(y, g)
+                    hbytes = m * spec.n * 5 + 4 * m
+                    hwarm = _time_ms(lambda: cr.pack_activations(y, g, out=hp))
+                    hcold = _time_ms(lambda: cr.pack_activations(y, g, out=hp), reps=10, flush=flush)
+                    emit(workload=w.name, kernel="pack", m=m, k=spec.n, x_dtype="f32", group_size=g,
+                         us_warm=round(hwarm * 1e3, 2), us_cold=round(hcold * 1e3, 2),
+                         gbps_cold=round(hbytes / (hcold * 1e-3) / 1e9, 1),
+                         hbm_frac_cold=round(hbytes / (hcold * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4))
+                    yd = torch.empty((m, dspec.n), dtype=torch.float32, device="cuda")
+                    td = _time_ms(lambda: cr.linear(hp, dqw, out=yd))
+                    dtops = 2.0 * m * dspec.n * spec.n / (td * 1e-3) / 1e12
+                    emit(workload=w.name, kernel="linear", linear=dspec.name, m=m, n=dspec.n,
+                         k=spec.n, group_size=g, gelu=False, us=round(td * 1e3, 2),
+                         tops=round(dtops, 1), mfma_frac=round(dtops / PEAK_INT8_TOPS, 4))
+                    del yd, hp
+                del y
+            if len(qws) > 1 and not w.gelu_chain:
+                ys = [torch.empty((m, q.q.shape[0]), dtype=torch.float32, device="cuda") for q in qws]
+                t = _time_ms(lambda: cr.linear_grouped(packed, qws, outs=ys))
+                n_total = sum(q.q.shape[0] for q in qws)
+                tops = 2.0 * m * n_total * k / (t * 1e-3) / 1e12
+                emit(workload=w.name, kernel="linear_grouped", n=n_total, m=m, k=k, group_size=g,
+                     us=round(t * 1e3, 2), tops=round(tops, 1), mfma_frac=round(tops / PEAK_INT8_TOPS, 4))
+                del ys
+            # The oracle on a row sample of the same workload (weights quantised
+            # offline and untimed, as on the device).
+            rows = min(m, 64)
+            qws_or = [orc.quantize_weights(wt, g) for wt in inp["weights"]]
+            n_total = sum(wt.shape[0] for wt in inp["weights"])
+            if w.gelu_chain:
+                qws_or, n_total = qws_or[:1], inp["weights"][0].shape[0]
+            emit(workload=w.name, kernel="cpu_baseline", group_size=g, kind="oracle",
+                 sample_rows=rows, cores=cores,
+                 tops=round(oracle_tops(inp["x64"][:rows], qws_or, g, n_total), 4))
+            del qws, packed
+        del x, inp
+        torch.cuda.empty_cache()
 
 
 def calibrate_copy():
@@ -127,6 +251,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.all_configs:
+        all_configs(args)
         return
 
     import torch
