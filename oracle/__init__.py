@@ -13,6 +13,9 @@ from .convrot_oracle import (  # noqa: F401
     h4,
     int_gemm,
     int_gemm_int64,
+    lora_correction,
+    lora_down,
+    lora_up,
     linear,
     log4_group,
     pack_activations,
@@ -22,5 +25,6 @@ from .convrot_oracle import (  # noqa: F401
     reference_linear_fp64,
     rotate,
     rotation_matrix,
+    round_bf16,
     round_half_away,
 )

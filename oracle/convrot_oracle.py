@@ -282,3 +282,52 @@ def reference_linear_fp64(x, w, bias=None) -> np.ndarray:
     if bias is not None:
         y = y + np.asarray(bias, dtype=np.float64)[None, :]
     return y
+
+
+# ---------------------------------------------------------------------------
+# 6. Low-rank adapter correction          [ICS, Backend support]
+# ---------------------------------------------------------------------------
+# The page applies LoRA-style adapters at run time: the convrot path computes
+# the base output, and the adapter computes its correction from the original,
+# *unrotated* activation and adds it.  The page gives no formula; the standard
+# low-rank form is used: with down weights A [r, K], up weights B [N, r] and a
+# scalar scale (alpha / r), the correction is  scale * (X A^T) B^T.
+#
+# Readings (listed in the design doc as well): the device computes in bfloat16
+# operands with float32 accumulation, so the oracle takes the same operand
+# values -- X (bfloat16 as given, float32 inputs rounded to bfloat16), A and B
+# as bfloat16 values -- and, like the device, rounds the rank-r intermediate
+# U = X A^T to bfloat16 (round to nearest even) before the up projection.
+# All sums are float64.
+
+
+def round_bf16(v: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value (ties to even), as float64.
+
+    bfloat16 keeps 8 significant bits: with v = f * 2**e, 0.5 <= |f| < 1, the
+    result is rint(f * 2**8) * 2**(e - 8) (np.rint rounds half to even).
+    Values are assumed finite and in bfloat16's normal range.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    f, e = np.frexp(v)
+    return np.ldexp(np.rint(np.ldexp(f, 8)), e - 8)
+
+
+def lora_down(x: np.ndarray, a: np.ndarray) -> np.ndarray:
+    """U = X A^T over the unrotated activation, rounded to bfloat16.
+
+    x: [M, K] (values already bfloat16), a: [r, K] bfloat16 values.
+    Returns float64 [M, r] holding bfloat16 values.
+    """
+    u = np.asarray(x, dtype=np.float64) @ np.asarray(a, dtype=np.float64).T
+    return round_bf16(u)
+
+
+def lora_up(u: np.ndarray, b: np.ndarray, scale: float) -> np.ndarray:
+    """The correction scale * U B^T (float64 [M, N]); b: [N, r]."""
+    return float(scale) * (np.asarray(u, dtype=np.float64) @ np.asarray(b, dtype=np.float64).T)
+
+
+def lora_correction(x, a, b, scale) -> np.ndarray:
+    """scale * (X A^T) B^T with the bfloat16 intermediate (see above)."""
+    return lora_up(lora_down(x, a), b, scale)

@@ -390,3 +390,54 @@ def test_activation_codes_use_division_not_reciprocal():
     q, s_row = orc.quantize_activation_rows(row)
     assert s_row[0] == s
     assert list(q[0, 1:]) == [want for _, want in found]
+
+
+# ---------------------------------------------------------------------------
+# Low-rank adapter correction (LoRA form, from the unrotated activation)
+# ---------------------------------------------------------------------------
+
+def test_round_bf16_matches_torch_conversion():
+    """Rounding to bfloat16 agrees with torch's float32 -> bfloat16 conversion
+    (round to nearest even) on float32 inputs, ties and neighbours included."""
+    import torch
+
+    rng = np.random.default_rng(11)
+    v = rng.standard_normal(20000).astype(np.float32) * np.float32(3.0)
+    # exact ties: bfloat16 value plus half a bfloat16 ulp
+    base = torch.from_numpy(v[:2000]).to(torch.bfloat16).to(torch.float32).numpy().astype(np.float64)
+    f, e = np.frexp(base)
+    ties = (base + np.ldexp(np.sign(base), e - 9)).astype(np.float32)
+    v = np.concatenate([v, ties])
+    want = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(orc.round_bf16(v.astype(np.float64)), want)
+
+
+def test_lora_rank_one_closed_form():
+    """A = e_j (one down row selecting feature j), B = ones: the correction is
+    scale * bf16(X[:, j]) in every output column."""
+    rng = np.random.default_rng(12)
+    x = orc.round_bf16(rng.standard_normal((5, 64)))
+    a = np.zeros((1, 64))
+    a[0, 17] = 1.0
+    b = np.ones((7, 1))
+    corr = orc.lora_correction(x, a, b, 0.5)
+    assert np.array_equal(corr, np.repeat(0.5 * x[:, 17:18], 7, axis=1))
+
+
+def test_lora_equals_merged_weight_update():
+    """scale (X A^T) B^T equals X (scale B A)^T (the merged low-rank weight)
+    up to the bfloat16 rounding of the intermediate X A^T."""
+    rng = np.random.default_rng(13)
+    x = orc.round_bf16(rng.standard_normal((9, 128)))
+    a = orc.round_bf16(rng.standard_normal((16, 128)) * 0.05)
+    b = orc.round_bf16(rng.standard_normal((24, 16)) * 0.05)
+    scale = 2.0
+    corr = orc.lora_correction(x, a, b, scale)
+    merged = x @ (scale * b @ a).T
+    u_exact = x @ a.T
+    bound = scale * (np.abs(u_exact) * 2.0 ** -8) @ np.abs(b).T  # half-ulp per U element
+    assert np.all(np.abs(corr - merged) <= bound + 1e-12)
+    assert not np.allclose(orc.lora_correction(x, a, b, -scale), merged)  # sign matters
+    # transposed operands would not even have matching shapes
+    with pytest.raises(ValueError):
+        orc.lora_correction(x, a.T, b, scale)
