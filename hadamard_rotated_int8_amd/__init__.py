@@ -38,12 +38,15 @@ ACT_GELU = 1
 MAX_K = 133136
 MAX_LOG4_GROUP = 7
 MAX_GROUPED = 8
+MAX_LORA_RANK = 128
 
 EXPORTED = (
     "convrot_quantize_weights",
     "convrot_pack_activations",
     "convrot_linear",
     "convrot_linear_grouped",
+    "convrot_lora_down",
+    "convrot_lora_up_add",
     "convrot_status_string",
     "convrot_version",
 )
@@ -101,6 +104,10 @@ def lib() -> ctypes.CDLL:
                                              ctypes.POINTER(ConvrotWeights), i32,
                                              ctypes.POINTER(vp), ctypes.POINTER(i64), i32, i32, vp]
         L.convrot_linear_grouped.restype = ctypes.c_int
+        L.convrot_lora_down.argtypes = [vp, i32, i64, i64, i64, vp, i32, vp, vp]
+        L.convrot_lora_down.restype = ctypes.c_int
+        L.convrot_lora_up_add.argtypes = [vp, vp, i64, i64, i32, ctypes.c_float, vp, i64, vp]
+        L.convrot_lora_up_add.restype = ctypes.c_int
         L.convrot_status_string.argtypes = [ctypes.c_int]
         L.convrot_status_string.restype = ctypes.c_char_p
         L.convrot_version.argtypes = []
@@ -141,6 +148,14 @@ def convrot_linear_grouped(x: ConvrotPacked, ws, ys, ldys, y_dtype, act=ACT_NONE
     larr = (ctypes.c_int64 * max(n, 1))(*ldys)
     return lib().convrot_linear_grouped(ctypes.byref(x), warr, n, yarr, larr, y_dtype, act,
                                         stream)
+
+
+def convrot_lora_down(x, x_dtype, m, k, ldx, a, rank, u, stream=None) -> int:
+    return lib().convrot_lora_down(x, x_dtype, m, k, ldx, a, rank, u, stream)
+
+
+def convrot_lora_up_add(u, b, m, n, rank, scale, y, ldy, stream=None) -> int:
+    return lib().convrot_lora_up_add(u, b, m, n, rank, scale, y, ldy, stream)
 
 
 def convrot_version() -> int:
@@ -263,3 +278,41 @@ def linear_grouped(x: PackedActivation, ws, outs=None, raw_i32: bool = False,
     if st != OK:
         raise ConvrotError(st, "convrot_linear_grouped")
     return outs
+
+
+def lora_down(x: torch.Tensor, a: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """U = X A^T (bfloat16 [m, rank]) for a low-rank adapter, on the unrotated X."""
+    _require_cuda(x, "x")
+    dt = {torch.float32: F32, torch.bfloat16: BF16}.get(x.dtype)
+    if dt is None or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a float32 or bfloat16 [m, k] tensor with unit column stride")
+    if a.dtype != torch.bfloat16 or a.dim() != 2 or not a.is_contiguous():
+        raise ValueError("a must be a contiguous bfloat16 [rank, k] tensor")
+    m, k = x.shape
+    rank = a.shape[0]
+    if a.shape[1] != k:
+        raise ValueError("a must have k columns")
+    if out is None:
+        out = torch.empty((m, rank), dtype=torch.bfloat16, device=x.device)
+    st = convrot_lora_down(_ptr(x), dt, m, k, x.stride(0), _ptr(a), rank, _ptr(out), _stream())
+    if st != OK:
+        raise ConvrotError(st, "convrot_lora_down")
+    return out
+
+
+def lora_up_add(u: torch.Tensor, b: torch.Tensor, y: torch.Tensor, scale: float) -> torch.Tensor:
+    """y += scale * U B^T in place (y float32 [m, n]); returns y."""
+    if u.dtype != torch.bfloat16 or b.dtype != torch.bfloat16 or not u.is_contiguous() \
+            or not b.is_contiguous():
+        raise ValueError("u and b must be contiguous bfloat16 tensors")
+    if y.dtype != torch.float32 or y.dim() != 2 or y.stride(1) != 1:
+        raise ValueError("y must be a float32 [m, n] tensor with unit column stride")
+    m, n = y.shape
+    rank = u.shape[1]
+    if u.shape[0] != m or b.shape != (n, rank):
+        raise ValueError("shapes: u [m, rank], b [n, rank], y [m, n]")
+    st = convrot_lora_up_add(_ptr(u), _ptr(b), m, n, rank, float(scale), _ptr(y), y.stride(0),
+                             _stream())
+    if st != OK:
+        raise ConvrotError(st, "convrot_lora_up_add")
+    return y

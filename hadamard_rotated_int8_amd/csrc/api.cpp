@@ -149,6 +149,45 @@ convrot_status convrot_pack_activations(const void* x, int32_t x_dtype, int64_t 
                                        out->scale, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+bool lora_rank_ok(int32_t rank) {
+  return rank >= 16 && rank <= CONVROT_MAX_LORA_RANK && rank % 16 == 0;
+}
+}  // namespace
+
+convrot_status convrot_lora_down(const void* x, int32_t x_dtype, int64_t m, int64_t k,
+                                 int64_t ldx, const void* a, int32_t rank, void* u,
+                                 void* stream) {
+  if (k < 1 || k > kMaxRows || m < 0 || m > kMaxRows || ldx < k || !lora_rank_ok(rank))
+    return CONVROT_ERR_SHAPE;
+  if (x_dtype != CONVROT_F32 && x_dtype != CONVROT_BF16) return CONVROT_ERR_DTYPE;
+  if (k % 16 != 0) return CONVROT_ERR_UNSUPPORTED;
+  if (m == 0) return CONVROT_OK;
+  if (!x || !a || !u) return CONVROT_ERR_NULL;
+  const int64_t esize = (x_dtype == CONVROT_F32) ? 4 : 2;
+  if (!aligned16(x) || !aligned16(a) || !aligned16(u) || (ldx * esize) % 16 != 0)
+    return CONVROT_ERR_UNSUPPORTED;
+  return from_hip(convrot::launch_lora_down(x, x_dtype == CONVROT_BF16, ldx, m, k,
+                                            static_cast<const uint16_t*>(a), rank,
+                                            static_cast<uint16_t*>(u),
+                                            static_cast<hipStream_t>(stream)));
+}
+
+convrot_status convrot_lora_up_add(const void* u, const void* b, int64_t m, int64_t n,
+                                   int32_t rank, float scale, float* y, int64_t ldy,
+                                   void* stream) {
+  if (m < 0 || m > kMaxRows || n < 0 || n > kMaxRows || ldy < n || !lora_rank_ok(rank))
+    return CONVROT_ERR_SHAPE;
+  if (m == 0 || n == 0) return CONVROT_OK;
+  if (((m + 127) / 128) * ((n + 127) / 128) > INT32_MAX) return CONVROT_ERR_SHAPE;
+  if (!u || !b || !y) return CONVROT_ERR_NULL;
+  if (!aligned16(u) || !aligned16(b) || (reinterpret_cast<uintptr_t>(y) & 3u) != 0)
+    return CONVROT_ERR_UNSUPPORTED;
+  return from_hip(convrot::launch_lora_up_add(static_cast<const uint16_t*>(u),
+                                              static_cast<const uint16_t*>(b), m, n, rank, scale,
+                                              y, ldy, static_cast<hipStream_t>(stream)));
+}
+
 convrot_status convrot_linear(const convrot_packed* x, const convrot_weights* w, void* y,
                               int32_t y_dtype, int64_t ldy, int32_t act, void* stream) {
   if (!x || !w) return CONVROT_ERR_NULL;

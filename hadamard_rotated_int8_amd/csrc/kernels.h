@@ -44,4 +44,13 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 
+constexpr int kLoraMaxRank = 128;  // adapter ranks 16, 32, ..., 128
+
+// U = X A^T (bfloat16 [m, r]); X [m, k] bf16 or float32, A bfloat16 [r, k].
+hipError_t launch_lora_down(const void* x, bool bf16, int64_t ldx, int64_t m, int64_t k,
+                            const uint16_t* a, int r, uint16_t* u, hipStream_t stream);
+// Y [m, n] (row stride ldy) += scale * U B^T; U bfloat16 [m, r], B bfloat16 [n, r].
+hipError_t launch_lora_up_add(const uint16_t* u, const uint16_t* b, int64_t m, int64_t n, int r,
+                              float scale, float* y, int64_t ldy, hipStream_t stream);
+
 }  // namespace convrot

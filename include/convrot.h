@@ -51,6 +51,7 @@ extern "C" {
 #define CONVROT_MAX_K 133136      /* largest k with k % 16 == 0 and k*127*127 < 2^31 */
 #define CONVROT_MAX_LOG4_GROUP 7  /* group sizes 1, 4, 16, ..., 16384 */
 #define CONVROT_MAX_GROUPED 8     /* weight matrices per convrot_linear_grouped call */
+#define CONVROT_MAX_LORA_RANK 128 /* adapter ranks 16, 32, ..., 128 */
 
 typedef enum convrot_status {
   CONVROT_OK = 0,
@@ -172,6 +173,44 @@ convrot_status convrot_linear(const convrot_packed* x, const convrot_weights* w,
 convrot_status convrot_linear_grouped(const convrot_packed* x, const convrot_weights* w,
                                       int32_t count, void* const* y, const int64_t* ldy,
                                       int32_t y_dtype, int32_t act, void* stream);
+
+/*
+ * Low-rank adapters ([ICS, Backend support]): LoRA-style adapters are applied
+ * at run time without touching the int8 weights; the convrot linear gives the
+ * base output and the adapter's correction, computed from the original
+ * UNROTATED activation X, is added to it.  In the low-rank form, with down
+ * weights A [rank, k], up weights B [n, rank] and a scale (alpha / rank):
+ *   Y += scale * (X A^T) B^T.
+ * Operands are bfloat16 with float32 accumulation; the rank-wide intermediate
+ * U = X A^T is kept as bfloat16.  (The page gives no formula or precision for
+ * the adapter path; this is the library's reading.)
+ *
+ * convrot_lora_down: U = X A^T.
+ *   x : device [m, k] of x_dtype (CONVROT_F32 or CONVROT_BF16), row stride
+ *       ldx >= k; float32 X is rounded to bfloat16 (nearest even)
+ *   a : device bfloat16 [rank, k], row stride k
+ *   u : device bfloat16 [m, rank], row stride rank (output)
+ *   rank a multiple of 16 in 16 .. CONVROT_MAX_LORA_RANK; k % 16 == 0;
+ *   x, a, u 16-byte aligned, ldx in whole 16-byte units.
+ * Errors: NULL, SHAPE, DTYPE, UNSUPPORTED, HIP.
+ */
+convrot_status convrot_lora_down(const void* x, int32_t x_dtype, int64_t m, int64_t k,
+                                 int64_t ldx, const void* a, int32_t rank, void* u,
+                                 void* stream);
+
+/*
+ * convrot_lora_up_add: Y[i, o] += scale * sum_j U[i, j] B[o, j].
+ *   u : device bfloat16 [m, rank] (from convrot_lora_down)
+ *   b : device bfloat16 [n, rank], row stride rank
+ *   y : device float32 [m, n], row stride ldy >= n (updated in place,
+ *       typically the output of convrot_linear)
+ *   rank as for convrot_lora_down; u and b 16-byte aligned, y 4-byte aligned;
+ *   ceil(m / 128) * ceil(n / 128) <= INT32_MAX (128 x 128 output tiles).
+ * Errors: NULL, SHAPE, UNSUPPORTED, HIP.
+ */
+convrot_status convrot_lora_up_add(const void* u, const void* b, int64_t m, int64_t n,
+                                   int32_t rank, float scale, float* y, int64_t ldy,
+                                   void* stream);
 
 /* A static, human-readable name for a status code (never NULL). */
 const char* convrot_status_string(convrot_status status);

@@ -190,3 +190,50 @@ def test_linear_grouped_validation():
     assert _grp(ydt=cr.I32, act=cr.ACT_GELU) == cr.ERR_DTYPE
     empty = [cr.ConvrotWeights(None, None, None, 0, 1024, 256) for _ in range(2)]
     assert _grp(ws=empty, ys=[None, None], ldys=[0, 0]) == cr.OK   # nothing to launch
+
+
+def _down(x=FAKE, dt=cr.BF16, m=64, k=1024, ldx=None, a=FAKE, r=32, u=FAKE):
+    return cr.convrot_lora_down(x, dt, m, k, k if ldx is None else ldx, a, r, u)
+
+
+def _up(u=FAKE, b=FAKE, m=64, n=512, r=32, y=FAKE, ldy=None):
+    return cr.convrot_lora_up_add(u, b, m, n, r, 0.5, y, n if ldy is None else ldy)
+
+
+def test_lora_rank_limits_match_header():
+    text = open(HEADER).read()
+    assert int(re.search(r"#define CONVROT_MAX_LORA_RANK (\d+)", text).group(1)) == cr.MAX_LORA_RANK
+
+
+@pytest.mark.parametrize("r", [0, 8, 15, 24, 136, 144, -16])
+def test_lora_rejects_bad_rank(r):
+    assert _down(r=r) == cr.ERR_SHAPE
+    assert _up(r=r) == cr.ERR_SHAPE
+
+
+def test_lora_down_validation():
+    assert _down(k=0) == cr.ERR_SHAPE
+    assert _down(m=-1) == cr.ERR_SHAPE
+    assert _down(ldx=512) == cr.ERR_SHAPE           # ldx < k
+    assert _down(dt=2) == cr.ERR_DTYPE
+    assert _down(k=1000) == cr.ERR_UNSUPPORTED       # k % 16
+    assert _down(x=None) == cr.ERR_NULL
+    assert _down(a=None) == cr.ERR_NULL
+    assert _down(u=None) == cr.ERR_NULL
+    assert _down(x=FAKE + 8) == cr.ERR_UNSUPPORTED   # misaligned
+    assert _down(u=FAKE + 2) == cr.ERR_UNSUPPORTED
+    assert _down(ldx=1028) == cr.ERR_UNSUPPORTED     # bf16 row stride not a 16-byte multiple
+    assert _down(m=0, x=None, a=None, u=None) == cr.OK  # empty: no work, no pointers needed
+
+
+def test_lora_up_add_validation():
+    assert _up(n=-1) == cr.ERR_SHAPE
+    assert _up(ldy=100) == cr.ERR_SHAPE              # ldy < n
+    assert _up(u=None) == cr.ERR_NULL
+    assert _up(b=None) == cr.ERR_NULL
+    assert _up(y=None) == cr.ERR_NULL
+    assert _up(u=FAKE + 4) == cr.ERR_UNSUPPORTED
+    assert _up(b=FAKE + 2) == cr.ERR_UNSUPPORTED
+    assert _up(y=FAKE + 2) == cr.ERR_UNSUPPORTED
+    assert _up(m=0, u=None, b=None, y=None) == cr.OK
+    assert _up(n=0, u=None, b=None, y=None) == cr.OK

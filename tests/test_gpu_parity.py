@@ -554,3 +554,108 @@ def test_linear_from_checkpoint(tmp_path):
         q_or, s_or, b, _ = mods[f"attn.{n}"]
         y_or = orc.linear(qx_or, sx_or, q_or, s_or, b)
         check_y(host(y), y_or, sx_or, s_or, wl.QKV.k, what=f"checkpoint {n}")
+
+
+# ---------------------------------------------------------------------------
+# Low-rank adapter correction (bf16 operands, float32 accumulation)
+# ---------------------------------------------------------------------------
+# U is rounded to bf16 on both sides, but the device rounds a float32 sum and
+# the oracle a float64 one, so an element of U may sit one bf16 unit apart
+# where the sum lies next to a rounding boundary.  Bounds:
+#   U: |dU| <= 2^-8 |U_or| + float32 accumulation error (2^-24 k sum|x||a|),
+#      on at most 1% of elements;
+#   Y: |dY| <= scale (2^-8 |U_or| + eps_U) |B|^T + 2^-22 (|Y0| + scale |U||B|^T),
+#      and the correction's aggregate L1 error <= 1e-3 of its L1 norm.
+LORA_U_MISMATCH_FRAC = 1e-2
+
+
+def _lora_case(m, k, n, rank, x_dtype, seed):
+    w = wl.Workload(name="lora", m=m, k=k, x_dtype=x_dtype, seed=seed, linears=(),
+                    channel_lognormal=True)
+    inp = wl.generate(w)
+    ad = wl.lora_adapter(k, n, rank, m=m, seed=seed + 100)
+    x64 = inp["x64"] if x_dtype == "bf16" else orc.round_bf16(inp["x64"])
+    return inp["x"], x64, ad
+
+
+def _check_lora(u_dev, y_dev, x64, ad, what):
+    a64, b64, scale = ad["a64"], ad["b64"], ad["scale"]
+    k = x64.shape[1]
+    u_or = orc.lora_down(x64, a64)
+    eps_u = 2.0**-24 * k * (np.abs(x64) @ np.abs(a64).T)
+    du = np.abs(u_dev.astype(np.float64) - u_or)
+    assert np.all(du <= 2.0**-8 * np.abs(u_or) + eps_u), f"{what}: U outside one bf16 unit"
+    frac = np.count_nonzero(du) / max(1, du.size)
+    assert frac <= LORA_U_MISMATCH_FRAC, f"{what}: {frac:.3%} of U differs"
+    corr = orc.lora_up(u_or, b64, scale)
+    y_or = ad["y0"].astype(np.float64) + corr
+    mag = scale * (np.abs(u_or) @ np.abs(b64).T)
+    bound = scale * ((2.0**-8 * np.abs(u_or) + eps_u) @ np.abs(b64).T) \
+        + 2.0**-22 * (np.abs(ad["y0"]) + mag)
+    err = np.abs(y_dev.astype(np.float64) - y_or)
+    assert np.all(err <= bound), f"{what}: Y bound exceeded by {np.max(err - bound):.3g}"
+    rel = err.sum() / max(np.abs(corr).sum(), 1e-30)
+    assert rel <= 1e-3, f"{what}: correction L1 error {rel:.3g}"
+    return frac, rel
+
+
+@pytest.mark.parametrize("m,k,n,rank,dt", [
+    (16, 1024, 512, 16, "f32"), (37, 1024, 700, 32, "bf16"), (300, 2048, 400, 48, "bf16"),
+    (257, 3072, 3072, 64, "f32"), (1000, 3072, 1100, 128, "bf16"), (64, 16, 129, 96, "bf16"),
+    (1, 4096, 33, 80, "f32"),
+])
+def test_lora_parity(m, k, n, rank, dt):
+    x, x64, ad = _lora_case(m, k, n, rank, dt, seed=m + rank)
+    _say(f"lora m={m} k={k} n={n} r={rank} {dt}")
+    u = cr.lora_down(dev(x), dev(ad["a"]))
+    y = dev(ad["y0"])
+    cr.lora_up_add(u, dev(ad["b"]), y, ad["scale"])
+    _check_lora(host(u.float()), host(y), x64, ad, f"lora {m}x{k}x{n} r{rank}")
+
+
+def test_lora_strided_x_and_y():
+    m, k, n, rank = 130, 1024, 300, 32
+    x, x64, ad = _lora_case(m, k, n, rank, "bf16", seed=7)
+    xs = torch.zeros((m, k + 64), dtype=torch.bfloat16)
+    xs[:, :k] = x
+    ys = torch.full((m, n + 5), 3.0, dtype=torch.float32)
+    ys[:, :n] = torch.from_numpy(ad["y0"])
+    _say("lora strided")
+    xd, yd = xs.cuda(), ys.cuda()
+    u = cr.lora_down(xd[:, :k], dev(ad["a"]))
+    cr.lora_up_add(u, dev(ad["b"]), yd[:, :n], ad["scale"])
+    yh = host(yd)
+    assert np.all(yh[:, n:] == 3.0), "padding columns of Y were written"
+    _check_lora(host(u.float()), yh[:, :n], x64, ad, "lora strided")
+
+
+def test_lora_on_convrot_output():
+    """The adapter's correction added to the convrot linear's output: the
+    complete adapted layer against the oracle's linear plus correction."""
+    inp = wl.generate(wl.QKV, m=320, n_limit=1000)
+    g, rank = 256, 64
+    wt, b = inp["weights"][0], inp["biases"][0]
+    ad = wl.lora_adapter(wl.QKV.k, wt.shape[0], rank, m=0, seed=11)
+    _say("lora on convrot output")
+    x = dev(inp["x"])
+    y = cr.linear(cr.pack_activations(x, g), _prep(wt, b, g))
+    cr.lora_up_add(cr.lora_down(x, dev(ad["a"])), dev(ad["b"]), y, ad["scale"])
+    qx_or, sx_or = orc.pack_activations(inp["x64"], g)
+    qw_or, sw_or = orc.quantize_weights(wt, g)
+    base = orc.linear(qx_or, sx_or, qw_or, sw_or, b)
+    corr = orc.lora_correction(inp["x64"], ad["a64"], ad["b64"], ad["scale"])
+    y_or = base + corr
+    bound = Y_ELEM * sx_or[:, None] * sw_or[None, :].astype(np.float64) * wl.QKV.k * 127 \
+        + 2.0**-7 * ad["scale"] * (np.abs(orc.lora_down(inp["x64"], ad["a64"])) @ np.abs(ad["b64"]).T)
+    err = np.abs(host(y).astype(np.float64) - y_or)
+    assert np.all(err <= bound), f"adapted layer: bound exceeded by {np.max(err - bound):.3g}"
+    assert err.sum() / np.abs(y_or).sum() <= Y_MEAN_REL
+
+
+def test_lora_empty():
+    a = torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda")
+    u = cr.lora_down(torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda"), a)
+    assert u.shape == (0, 16)
+    y = torch.zeros((0, 8), device="cuda")
+    cr.lora_up_add(u, torch.zeros((8, 16), dtype=torch.bfloat16, device="cuda"), y, 1.0)
+    torch.cuda.synchronize()

@@ -14,6 +14,9 @@ the fixed order X -> outlier columns or channel scales -> each W -> each b.
   float32 draw once, round-to-nearest-even, with torch on the CPU; the float64
   view handed to the oracle is the exact value of those bf16 bits.
 * W ~ N(0, 0.02) float32 (0.02 is the standard deviation), b ~ N(0, 0.01).
+* Low-rank adapters (``lora_adapter``): A ~ N(0, 1) / sqrt(K) and
+  B ~ N(0, 0.02), both rounded to bf16 once; scale = alpha / rank with
+  alpha = 16; a base output Y0 ~ N(0, 1) float32 for the in-place update.
 
 Shapes are those of DiT blocks (attention projections, an MLP pair, a long
 video-token sequence); real checkpoints and prompts are not used.
@@ -157,6 +160,21 @@ def generate(w: Workload, m: int | None = None, n_limit: int | None = None,
     else:
         raise ValueError(w.x_dtype)
     return {"x": x, "x64": x64, "weights": weights, "biases": biases}
+
+
+def lora_adapter(k: int, n: int, rank: int, m: int = 0, seed: int = 0, alpha: float = 16.0) -> dict:
+    """Draw a rank-``rank`` adapter for a [n, k] linear (and a base output [m, n]).
+
+    Returns a (torch bf16 CPU tensor [rank, k]), a64 (float64, same values),
+    b, b64 ([n, rank]), y0 (float32 numpy [m, n]) and scale = alpha / rank.
+    """
+    rng = np.random.default_rng(seed)
+    a32 = rng.standard_normal((rank, k), dtype=np.float32) * np.float32(1.0 / np.sqrt(k))
+    b32 = rng.standard_normal((n, rank), dtype=np.float32) * np.float32(0.02)
+    y0 = rng.standard_normal((m, n), dtype=np.float32)
+    a, a64 = _bf16_round(a32)
+    b, b64 = _bf16_round(b32)
+    return {"a": a, "a64": a64, "b": b, "b64": b64, "y0": y0, "scale": alpha / rank}
 
 
 def crafted_rotated_rows(group_size: int, k: int, rows: int, seed: int = 0):
