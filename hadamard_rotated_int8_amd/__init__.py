@@ -47,6 +47,7 @@ EXPORTED = (
     "convrot_linear_grouped",
     "convrot_lora_down",
     "convrot_lora_up_add",
+    "convrot_linear_lora",
     "convrot_status_string",
     "convrot_version",
 )
@@ -79,6 +80,15 @@ class ConvrotWeights(ctypes.Structure):
     ]
 
 
+class ConvrotLora(ctypes.Structure):
+    _fields_ = [
+        ("u", ctypes.c_void_p),
+        ("b", ctypes.c_void_p),
+        ("ldu", ctypes.c_int64),
+        ("rank", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -104,10 +114,16 @@ def lib() -> ctypes.CDLL:
                                              ctypes.POINTER(ConvrotWeights), i32,
                                              ctypes.POINTER(vp), ctypes.POINTER(i64), i32, i32, vp]
         L.convrot_linear_grouped.restype = ctypes.c_int
-        L.convrot_lora_down.argtypes = [vp, i32, i64, i64, i64, vp, i32, vp, vp]
+        L.convrot_lora_down.argtypes = [vp, i32, i64, i64, i64, vp, i32, ctypes.c_float, vp, i64,
+                                        vp]
         L.convrot_lora_down.restype = ctypes.c_int
-        L.convrot_lora_up_add.argtypes = [vp, vp, i64, i64, i32, ctypes.c_float, vp, i64, vp]
+        L.convrot_lora_up_add.argtypes = [vp, i64, vp, i64, i64, i32, vp, i64, vp]
         L.convrot_lora_up_add.restype = ctypes.c_int
+        L.convrot_linear_lora.argtypes = [ctypes.POINTER(ConvrotPacked),
+                                          ctypes.POINTER(ConvrotWeights),
+                                          ctypes.POINTER(ConvrotLora), i32, ctypes.POINTER(vp),
+                                          ctypes.POINTER(i64), i32, vp]
+        L.convrot_linear_lora.restype = ctypes.c_int
         L.convrot_status_string.argtypes = [ctypes.c_int]
         L.convrot_status_string.restype = ctypes.c_char_p
         L.convrot_version.argtypes = []
@@ -150,12 +166,22 @@ def convrot_linear_grouped(x: ConvrotPacked, ws, ys, ldys, y_dtype, act=ACT_NONE
                                         stream)
 
 
-def convrot_lora_down(x, x_dtype, m, k, ldx, a, rank, u, stream=None) -> int:
-    return lib().convrot_lora_down(x, x_dtype, m, k, ldx, a, rank, u, stream)
+def convrot_lora_down(x, x_dtype, m, k, ldx, a, rank, scale, u, ldu, stream=None) -> int:
+    return lib().convrot_lora_down(x, x_dtype, m, k, ldx, a, rank, scale, u, ldu, stream)
 
 
-def convrot_lora_up_add(u, b, m, n, rank, scale, y, ldy, stream=None) -> int:
-    return lib().convrot_lora_up_add(u, b, m, n, rank, scale, y, ldy, stream)
+def convrot_lora_up_add(u, ldu, b, m, n, rank, y, ldy, stream=None) -> int:
+    return lib().convrot_lora_up_add(u, ldu, b, m, n, rank, y, ldy, stream)
+
+
+def convrot_linear_lora(x: ConvrotPacked, ws, loras, ys, ldys, act=ACT_NONE, stream=None) -> int:
+    """ws: ConvrotWeights; loras: ConvrotLora (rank 0 = none); ys, ldys as for grouped."""
+    n = len(ws)
+    warr = (ConvrotWeights * max(n, 1))(*ws)
+    larr_ = (ConvrotLora * max(n, 1))(*loras)
+    yarr = (ctypes.c_void_p * max(n, 1))(*ys)
+    ldarr = (ctypes.c_int64 * max(n, 1))(*ldys)
+    return lib().convrot_linear_lora(ctypes.byref(x), warr, larr_, n, yarr, ldarr, act, stream)
 
 
 def convrot_version() -> int:
@@ -280,8 +306,13 @@ def linear_grouped(x: PackedActivation, ws, outs=None, raw_i32: bool = False,
     return outs
 
 
-def lora_down(x: torch.Tensor, a: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """U = X A^T (bfloat16 [m, rank]) for a low-rank adapter, on the unrotated X."""
+def lora_down(x: torch.Tensor, a: torch.Tensor, scale: float,
+              out: torch.Tensor | None = None) -> torch.Tensor:
+    """U = bf16(scale X A^T) for a low-rank adapter, on the unrotated X.
+
+    ``out`` may be a column slice of a wider bfloat16 buffer (unit column
+    stride, row stride a multiple of 8); by default a new [m, rank] tensor.
+    """
     _require_cuda(x, "x")
     dt = {torch.float32: F32, torch.bfloat16: BF16}.get(x.dtype)
     if dt is None or x.dim() != 2 or x.stride(1) != 1:
@@ -294,25 +325,65 @@ def lora_down(x: torch.Tensor, a: torch.Tensor, out: torch.Tensor | None = None)
         raise ValueError("a must have k columns")
     if out is None:
         out = torch.empty((m, rank), dtype=torch.bfloat16, device=x.device)
-    st = convrot_lora_down(_ptr(x), dt, m, k, x.stride(0), _ptr(a), rank, _ptr(out), _stream())
+    if out.dtype != torch.bfloat16 or out.shape != (m, rank) or out.stride(1) != 1:
+        raise ValueError("out must be a bfloat16 [m, rank] view with unit column stride")
+    st = convrot_lora_down(_ptr(x), dt, m, k, x.stride(0), _ptr(a), rank, float(scale), _ptr(out),
+                           out.stride(0), _stream())
     if st != OK:
         raise ConvrotError(st, "convrot_lora_down")
     return out
 
 
-def lora_up_add(u: torch.Tensor, b: torch.Tensor, y: torch.Tensor, scale: float) -> torch.Tensor:
-    """y += scale * U B^T in place (y float32 [m, n]); returns y."""
-    if u.dtype != torch.bfloat16 or b.dtype != torch.bfloat16 or not u.is_contiguous() \
-            or not b.is_contiguous():
-        raise ValueError("u and b must be contiguous bfloat16 tensors")
+def _check_u(u: torch.Tensor, m: int):
+    if u.dtype != torch.bfloat16 or u.dim() != 2 or u.stride(1) != 1 or u.shape[0] != m:
+        raise ValueError("u must be a bfloat16 [m, rank] tensor with unit column stride")
+
+
+def lora_up_add(u: torch.Tensor, b: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
+    """y += U B^T in place (y float32 [m, n]), a separate pass; returns y."""
     if y.dtype != torch.float32 or y.dim() != 2 or y.stride(1) != 1:
         raise ValueError("y must be a float32 [m, n] tensor with unit column stride")
     m, n = y.shape
+    _check_u(u, m)
     rank = u.shape[1]
-    if u.shape[0] != m or b.shape != (n, rank):
-        raise ValueError("shapes: u [m, rank], b [n, rank], y [m, n]")
-    st = convrot_lora_up_add(_ptr(u), _ptr(b), m, n, rank, float(scale), _ptr(y), y.stride(0),
+    if b.dtype != torch.bfloat16 or not b.is_contiguous() or b.shape != (n, rank):
+        raise ValueError("b must be a contiguous bfloat16 [n, rank] tensor")
+    st = convrot_lora_up_add(_ptr(u), u.stride(0), _ptr(b), m, n, rank, _ptr(y), y.stride(0),
                              _stream())
     if st != OK:
         raise ConvrotError(st, "convrot_lora_up_add")
     return y
+
+
+def linear_lora(x: PackedActivation, ws, adapters, outs=None, gelu: bool = False):
+    """Grouped linears with each weight's adapter added in the epilogue.
+
+    adapters: one (u, b) pair per weight -- u from ``lora_down`` (bfloat16
+    [m, rank]), b bfloat16 [n, rank] -- or None for a weight without one.
+    Returns the float32 outputs act(Y + U B^T).
+    """
+    m = x.q.shape[0]
+    if len(adapters) != len(ws):
+        raise ValueError("one adapter (or None) per weight")
+    if outs is None:
+        outs = [torch.empty((m, w.q.shape[0]), dtype=torch.float32, device=x.q.device) for w in ws]
+    loras = []
+    for w, ad in zip(ws, adapters):
+        if ad is None:
+            loras.append(ConvrotLora(None, None, 0, 0))
+            continue
+        u, b = ad
+        _check_u(u, m)
+        rank = u.shape[1]
+        if b.dtype != torch.bfloat16 or not b.is_contiguous() or b.shape != (w.q.shape[0], rank):
+            raise ValueError("b must be a contiguous bfloat16 [n, rank] tensor")
+        loras.append(ConvrotLora(_ptr(u), _ptr(b), u.stride(0), rank))
+    for o in outs:
+        if o.dtype != torch.float32 or o.dim() != 2 or o.stride(1) != 1:
+            raise ValueError("an output has the wrong dtype or layout")
+    st = convrot_linear_lora(x.as_c(), [w.as_c() for w in ws], loras, [_ptr(o) for o in outs],
+                             [o.stride(0) for o in outs], ACT_GELU if gelu else ACT_NONE,
+                             _stream())
+    if st != OK:
+        raise ConvrotError(st, "convrot_linear_lora")
+    return outs

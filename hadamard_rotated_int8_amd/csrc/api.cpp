@@ -64,9 +64,32 @@ convrot_status check_weight(const convrot_packed* x, const convrot_weights* w, v
   return CONVROT_OK;
 }
 
+bool lora_rank_ok(int32_t rank) {
+  return rank >= 16 && rank <= CONVROT_MAX_LORA_RANK && rank % 16 == 0;
+}
+
+// Validate one weight's adapter (rank 0: none) and fill its launch slot.
+convrot_status check_lora(const convrot_lora* l, int64_t m, int64_t n, convrot::GemmWeight* out) {
+  if (!l) return CONVROT_ERR_NULL;
+  if (l->rank == 0) return CONVROT_OK;
+  if (!lora_rank_ok(l->rank) || l->ldu < l->rank || l->ldu > convrot::kLoraMaxLdu)
+    return CONVROT_ERR_SHAPE;
+  if (l->ldu % 8 != 0) return CONVROT_ERR_UNSUPPORTED;
+  if (m > 0 && n > 0) {
+    if (!l->u || !l->b) return CONVROT_ERR_NULL;
+    if (!aligned16(l->u) || !aligned16(l->b)) return CONVROT_ERR_UNSUPPORTED;
+  }
+  out->lu = static_cast<const uint16_t*>(l->u);
+  out->lb = static_cast<const uint16_t*>(l->b);
+  out->ldu = l->ldu;
+  out->rank = l->rank;
+  return CONVROT_OK;
+}
+
+// lora: NULL, or one adapter per weight (the float32-output fused path).
 convrot_status run_linear(const convrot_packed* x, const convrot_weights* const* w, int32_t count,
                           void* const* y, const int64_t* ldy, int32_t y_dtype, int32_t act,
-                          void* stream) {
+                          void* stream, const convrot_lora* lora = nullptr) {
   if (!x) return CONVROT_ERR_NULL;
   int log4g = 0;
   convrot_status st = check_k_group(x->k, x->group_size, &log4g);
@@ -82,9 +105,15 @@ convrot_status run_linear(const convrot_packed* x, const convrot_weights* const*
   a.count = 0;
   a.raw_i32 = (y_dtype == CONVROT_I32);
   a.gelu = (act == CONVROT_ACT_GELU);
+  a.lora = lora != nullptr;
   for (int32_t i = 0; i < count; ++i) {
+    a.w[a.count] = convrot::GemmWeight{};  // (a skipped empty weight may have filled it)
     st = check_weight(x, w[i], y[i], ldy[i], y_dtype, &a.w[a.count]);
     if (st != CONVROT_OK) return st;
+    if (lora) {
+      st = check_lora(&lora[i], x->m, w[i]->n, &a.w[a.count]);
+      if (st != CONVROT_OK) return st;
+    }
     if (w[i]->n > 0) ++a.count;  // empty weights launch nothing
   }
   if (x->m == 0 || a.count == 0) return CONVROT_OK;
@@ -149,43 +178,39 @@ convrot_status convrot_pack_activations(const void* x, int32_t x_dtype, int64_t 
                                        out->scale, static_cast<hipStream_t>(stream)));
 }
 
-namespace {
-bool lora_rank_ok(int32_t rank) {
-  return rank >= 16 && rank <= CONVROT_MAX_LORA_RANK && rank % 16 == 0;
-}
-}  // namespace
-
 convrot_status convrot_lora_down(const void* x, int32_t x_dtype, int64_t m, int64_t k,
-                                 int64_t ldx, const void* a, int32_t rank, void* u,
-                                 void* stream) {
-  if (k < 1 || k > kMaxRows || m < 0 || m > kMaxRows || ldx < k || !lora_rank_ok(rank))
+                                 int64_t ldx, const void* a, int32_t rank, float scale, void* u,
+                                 int64_t ldu, void* stream) {
+  if (k < 1 || k > kMaxRows || m < 0 || m > kMaxRows || ldx < k || !lora_rank_ok(rank) ||
+      ldu < rank || ldu > convrot::kLoraMaxLdu)
     return CONVROT_ERR_SHAPE;
   if (x_dtype != CONVROT_F32 && x_dtype != CONVROT_BF16) return CONVROT_ERR_DTYPE;
-  if (k % 16 != 0) return CONVROT_ERR_UNSUPPORTED;
+  if (k % 16 != 0 || ldu % 8 != 0) return CONVROT_ERR_UNSUPPORTED;
   if (m == 0) return CONVROT_OK;
   if (!x || !a || !u) return CONVROT_ERR_NULL;
   const int64_t esize = (x_dtype == CONVROT_F32) ? 4 : 2;
   if (!aligned16(x) || !aligned16(a) || !aligned16(u) || (ldx * esize) % 16 != 0)
     return CONVROT_ERR_UNSUPPORTED;
   return from_hip(convrot::launch_lora_down(x, x_dtype == CONVROT_BF16, ldx, m, k,
-                                            static_cast<const uint16_t*>(a), rank,
-                                            static_cast<uint16_t*>(u),
+                                            static_cast<const uint16_t*>(a), rank, scale,
+                                            static_cast<uint16_t*>(u), ldu,
                                             static_cast<hipStream_t>(stream)));
 }
 
-convrot_status convrot_lora_up_add(const void* u, const void* b, int64_t m, int64_t n,
-                                   int32_t rank, float scale, float* y, int64_t ldy,
-                                   void* stream) {
-  if (m < 0 || m > kMaxRows || n < 0 || n > kMaxRows || ldy < n || !lora_rank_ok(rank))
+convrot_status convrot_lora_up_add(const void* u, int64_t ldu, const void* b, int64_t m,
+                                   int64_t n, int32_t rank, float* y, int64_t ldy, void* stream) {
+  if (m < 0 || m > kMaxRows || n < 0 || n > kMaxRows || ldy < n || !lora_rank_ok(rank) ||
+      ldu < rank || ldu > convrot::kLoraMaxLdu)
     return CONVROT_ERR_SHAPE;
+  if (ldu % 8 != 0) return CONVROT_ERR_UNSUPPORTED;
   if (m == 0 || n == 0) return CONVROT_OK;
   if (((m + 127) / 128) * ((n + 127) / 128) > INT32_MAX) return CONVROT_ERR_SHAPE;
   if (!u || !b || !y) return CONVROT_ERR_NULL;
   if (!aligned16(u) || !aligned16(b) || (reinterpret_cast<uintptr_t>(y) & 3u) != 0)
     return CONVROT_ERR_UNSUPPORTED;
-  return from_hip(convrot::launch_lora_up_add(static_cast<const uint16_t*>(u),
-                                              static_cast<const uint16_t*>(b), m, n, rank, scale,
-                                              y, ldy, static_cast<hipStream_t>(stream)));
+  return from_hip(convrot::launch_lora_up_add(static_cast<const uint16_t*>(u), ldu,
+                                              static_cast<const uint16_t*>(b), m, n, rank, y, ldy,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 convrot_status convrot_linear(const convrot_packed* x, const convrot_weights* w, void* y,
@@ -205,6 +230,16 @@ convrot_status convrot_linear_grouped(const convrot_packed* x, const convrot_wei
   const convrot_weights* ws[CONVROT_MAX_GROUPED];
   for (int32_t i = 0; i < count; ++i) ws[i] = &w[i];
   return run_linear(x, ws, count, y, ldy, y_dtype, act, stream);
+}
+
+convrot_status convrot_linear_lora(const convrot_packed* x, const convrot_weights* w,
+                                   const convrot_lora* lora, int32_t count, void* const* y,
+                                   const int64_t* ldy, int32_t act, void* stream) {
+  if (!x || !w || !lora || !y || !ldy) return CONVROT_ERR_NULL;
+  if (count < 1 || count > CONVROT_MAX_GROUPED) return CONVROT_ERR_SHAPE;
+  const convrot_weights* ws[CONVROT_MAX_GROUPED];
+  for (int32_t i = 0; i < count; ++i) ws[i] = &w[i];
+  return run_linear(x, ws, count, y, ldy, CONVROT_F32, act, stream, lora);
 }
 
 }  // extern "C"

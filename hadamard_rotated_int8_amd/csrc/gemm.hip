@@ -53,6 +53,13 @@
 //   * Tiles are dealt so that the workgroups of one XCD (workgroups go to the
 //     8 XCDs round robin) work on neighbouring tile rows and columns, which
 //     they then share in that XCD's L2.
+//   * Low-rank adapters (the page's section "Backend support": a correction
+//     from the unrotated X added to the output): in the adapter modes the
+//     finished tile's accumulators are turned into float32 Y values in place
+//     (A s_x s_w + b) at the tile end, and the adapter's U B^T is added by
+//     bf16 MFMAs that take those registers as their accumulator input; the
+//     rank/16 MFMAs per 32x32 block share the int8 accumulator layout.  The
+//     deferred stores then write the finished values.
 #include <mutex>
 #include <type_traits>
 #include <utility>
@@ -66,6 +73,8 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBM = 256;
@@ -79,7 +88,7 @@ constexpr int kVmMax = 63;     // largest vmcnt a wait can name
 constexpr int kBufferWord3 = 0x00020000;
 constexpr unsigned kOutOfRange = 0x80000000u;  // an offset past every resource
 
-enum { kModeF32 = 0, kModeGelu = 1, kModeI32 = 2 };
+enum { kModeF32 = 0, kModeGelu = 1, kModeI32 = 2, kModeLora = 3, kModeLoraGelu = 4 };
 
 template <int BN>
 struct Cfg {
@@ -122,6 +131,9 @@ struct Seg {
   int64_t ldy;
   int n;
   int tn0;  // first global tile column of this weight
+  const uint16_t* lu;  // adapter: U bfloat16 [M, ldu], B bfloat16 [n, rank]
+  const uint16_t* lb;
+  int ldu, rank;       // rank 0: no adapter
 };
 
 struct GemmParams {
@@ -225,6 +237,11 @@ template <int BN, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p) {
   using C = Cfg<BN>;
   constexpr int FM = C::FM, FN = C::FN, NV = C::NV, NG = C::NG, NSS = C::NSS;
+  constexpr bool LORA = MODE == kModeLora || MODE == kModeLoraGelu;
+  constexpr bool GELU = MODE == kModeGelu || MODE == kModeLoraGelu;
+  // Scales and bias applied when a value is stored (otherwise the pending
+  // values are raw int32 results or finished float32 values).
+  constexpr bool SCALE_AT_STORE = MODE == kModeF32 || MODE == kModeGelu;
   __shared__ __attribute__((aligned(1024))) int8_t smem[C::LDS];
 
   const int lane = threadIdx.x & 63;
@@ -410,9 +427,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
                                                                4 * (lane >> 5)) * 4);
   };
   auto scaled_with = [&](int raw, float sx, float sw, float b) -> float {
-    if (MODE == kModeI32) return __int_as_float(raw);
-    float v = __builtin_fmaf((float)raw * sx, sw, b);
-    if (MODE == kModeGelu) v = gelu_erf(v);
+    if constexpr (MODE == kModeI32) return __int_as_float(raw);
+    float v = SCALE_AT_STORE ? __builtin_fmaf((float)raw * sx, sw, b) : __int_as_float(raw);
+    if constexpr (GELU) v = gelu_erf(v);
     return v;
   };
   auto scaled = [&](int raw, float sx, int j) -> float { return scaled_with(raw, sx, pd_sw[j], pd_b[j]); };
@@ -502,8 +519,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
     // ahead (only two are live at a time).
     // s_w and b of the lane's columns, from the tile's parameter buffer
     // (kept in LDS, not in registers, between the steps that store).
-    float gsw[FN], gb[FN];
-    if constexpr (STORE && MODE != kModeI32) {
+    float gsw[FN] = {}, gb[FN] = {};
+    if constexpr (STORE && SCALE_AT_STORE) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int nl = (wave & 1) * C::WN + j * 32 + (lane & 31);
@@ -528,9 +545,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
         }
       }
     };
-    f32x2 gsx[C::GSUB];
+    f32x2 gsx[C::GSUB] = {};
     auto read_gsx = [&](int kk) {
-      if constexpr (STORE) {
+      if constexpr (STORE && SCALE_AT_STORE) {
 #pragma unroll
         for (int g = 0; g < C::GSUB; ++g)
           gsx[g] = *reinterpret_cast<const f32x2*>(
@@ -624,6 +641,96 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
     cur_w = nxt_w;
   };
 
+  // Adapter epilogue of tile t_it: its accumulators become float32 Y values
+  // (A s_x s_w + b, from the tile's parameter buffer, the rounding of the
+  // store-time path), and U B^T is accumulated onto them.  U and B fragments
+  // come straight from global memory (L2) by buffer loads whose resources
+  // span the tile's valid rows, so rows past M or n read as zero; two 16-wide
+  // rank slices are requested at a time, then their MFMAs run.
+  auto lora_epilogue = [&](int t_it) __attribute__((always_inline)) {
+    reload_uniforms();
+    // Lane-derived offsets are formed here, from a copy the compiler cannot
+    // see through, rather than hoisted out of the tile loop (live across
+    // the K loop they would spill).
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    const TileInfo ti = tile_info<BN>(p, slot + t_it * G);
+    const Seg& sg = p.seg[ti.s];
+    const int8_t* par = smem + C::PAR0 + (t_it & 1) * C::PARB;
+    const int wm = wave >> 1, wn = wave & 1;
+    const bool has_b = sg.bias != nullptr;
+    float sw[FN], bb[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int nl = wn * C::WN + j * 32 + (lane & 31);
+      sw[j] = *reinterpret_cast<const float*>(par + (kBM + nl) * 4);
+      const float bv = *reinterpret_cast<const float*>(par + (kBM + BN + nl) * 4);
+      bb[j] = has_b ? bv : 0.f;
+    }
+    // Register e of block (i, j) is row 8 (e / 4) + e % 4 + 4 (lane / 32) of
+    // row block i: four consecutive rows per f32x4 of s_x.
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 sx4 = *reinterpret_cast<const f32x4*>(
+            par + (wm * 128 + i * 32 + 8 * r4 + 4 * (lane >> 5)) * 4);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int e = 4 * r4 + rr;
+            acc[i][j][e] = __float_as_int(__builtin_fmaf((float)acc[i][j][e] * sx4[rr], sw[j], bb[j]));
+          }
+      }
+    const int rank = sg.rank;
+    if (rank > 0) {
+      const int rows = M - ti.m0 < kBM ? M - ti.m0 : kBM;
+      const int cols = sg.n - ti.n0 < BN ? sg.n - ti.n0 : BN;
+      const int ldu = sg.ldu;
+      const __amdgpu_buffer_rsrc_t ur = buffer_rsrc(sg.lu + (int64_t)ti.m0 * ldu, rows * ldu * 2);
+      const __amdgpu_buffer_rsrc_t br = buffer_rsrc(sg.lb + (int64_t)ti.n0 * rank, cols * rank * 2);
+      // Lane l: row l % 32 of a 32-row block, bf16 elements 8 (l / 32) .. +7
+      // of a 16-wide rank slice (both operands; the sum runs over all 16).
+      const unsigned uoff = unsigned(((wm * 128 + (lane & 31)) * ldu + 8 * (lane >> 5)) * 2);
+      const unsigned boff = unsigned(((wn * C::WN + (lane & 31)) * rank + 8 * (lane >> 5)) * 2);
+      constexpr int KS = 2;  // 16-wide rank slices per batch of loads
+      for (int k0 = 0; k0 < rank; k0 += 16 * KS) {
+        v4i uf[KS][FM], bfr[KS][FN];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (k0 + 16 * ks < rank) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+              uf[ks][i] = __builtin_bit_cast(
+                  v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                           ur, uoff + unsigned((i * 32 * ldu + k0 + 16 * ks) * 2), 0, 0));
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+              bfr[ks][j] = __builtin_bit_cast(
+                  v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                           br, boff + unsigned((j * 32 * rank + k0 + 16 * ks) * 2), 0, 0));
+          }
+        }
+        waitvm_c<0>();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (k0 + 16 * ks < rank) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+              for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_bit_cast(
+                    v16i, __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                              __builtin_bit_cast(bf16x8, uf[ks][i]),
+                              __builtin_bit_cast(bf16x8, bfr[ks][j]),
+                              __builtin_bit_cast(f32x16, acc[i][j]), 0, 0, 0));
+          }
+        }
+      }
+    }
+  };
+
   for (int it = 0; it < ntiles; ++it) {
     // Tile prologue: the next tile's operand rows (the load streams enter it
     // during this tile's last steps) and this tile's scales and bias.
@@ -667,12 +774,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
     // The tile is complete and the previous one fully stored: move the
     // accumulators into pend.  The tile's parameters were requested in its
     // prologue and have been waited for since.
+    if constexpr (LORA) lora_epilogue(it);
 #pragma unroll
     for (int q = 0; q < NG; ++q)
 #pragma unroll
       for (int e = 0; e < NV; ++e)
       {
-        const int v = acc[q >> 3][e >> 1][4 * ((q >> 1) & 3) + 2 * (q & 1) + (e & 1)];
+        int v = acc[q >> 3][e >> 1][4 * ((q >> 1) & 3) + 2 * (q & 1) + (e & 1)];
+        // Finished values only feed stores, which could take them from the
+        // accumulator registers; keep them in ordinary VGPRs, which is where
+        // the register file has room next to the running tile.
+        if constexpr (LORA) asm volatile("" : "+v"(v));
         if (q >= NG - C::NPK)
           *park_slot(q, e) = v;
         else
@@ -762,6 +874,15 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     s.ldy = a.w[i].ldy;
     s.n = int(a.w[i].n);
     s.tn0 = 0;
+    s.lu = a.w[i].lu;
+    s.lb = a.w[i].lb;
+    s.ldu = int(a.w[i].ldu);
+    s.rank = a.lora ? a.w[i].rank : 0;
+  }
+  if (a.lora) {
+    if (a.raw_i32) return hipErrorInvalidValue;
+    if (a.gelu) return launch_t<kBN, kModeLoraGelu>(p, stream);
+    return launch_t<kBN, kModeLora>(p, stream);
   }
   if (a.raw_i32) return launch_t<kBN, kModeI32>(p, stream);
   if (a.gelu) return launch_t<kBN, kModeGelu>(p, stream);

@@ -31,6 +31,11 @@ struct GemmWeight {
   const float* bias;  // [n] or nullptr
   void* y;            // [m, ldy] float32 or int32
   int64_t n, ldy;
+  // Low-rank adapter added in the epilogue (rank 0: none): Y += U B^T.
+  const uint16_t* lu = nullptr;  // U bfloat16 [m, ldu]
+  const uint16_t* lb = nullptr;  // B bfloat16 [n, rank]
+  int64_t ldu = 0;
+  int rank = 0;
 };
 
 struct GemmArgs {
@@ -41,16 +46,21 @@ struct GemmArgs {
   GemmWeight w[kMaxGemmGroup];
   bool raw_i32;
   bool gelu;
+  bool lora = false;  // add each weight's adapter (GemmWeight::rank > 0) in the epilogue
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 
-constexpr int kLoraMaxRank = 128;  // adapter ranks 16, 32, ..., 128
+constexpr int kLoraMaxRank = 128;        // adapter ranks 16, 32, ..., 128
+constexpr int64_t kLoraMaxLdu = 1 << 20;  // U row stride limit (32-bit buffer offsets)
 
-// U = X A^T (bfloat16 [m, r]); X [m, k] bf16 or float32, A bfloat16 [r, k].
+// U = bf16(scale X A^T) (bfloat16 [m, r], row stride ldu); X [m, k] bf16 or
+// float32, A bfloat16 [r, k].
 hipError_t launch_lora_down(const void* x, bool bf16, int64_t ldx, int64_t m, int64_t k,
-                            const uint16_t* a, int r, uint16_t* u, hipStream_t stream);
-// Y [m, n] (row stride ldy) += scale * U B^T; U bfloat16 [m, r], B bfloat16 [n, r].
-hipError_t launch_lora_up_add(const uint16_t* u, const uint16_t* b, int64_t m, int64_t n, int r,
-                              float scale, float* y, int64_t ldy, hipStream_t stream);
+                            const uint16_t* a, int r, float scale, uint16_t* u, int64_t ldu,
+                            hipStream_t stream);
+// Y [m, n] (row stride ldy) += U B^T; U bfloat16 [m, r] (row stride ldu),
+// B bfloat16 [n, r].
+hipError_t launch_lora_up_add(const uint16_t* u, int64_t ldu, const uint16_t* b, int64_t m,
+                              int64_t n, int r, float* y, int64_t ldy, hipStream_t stream);
 
 }  // namespace convrot

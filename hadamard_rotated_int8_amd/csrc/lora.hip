@@ -5,8 +5,9 @@
 // the base output, and the adapter's correction is computed from the
 // original, unrotated activation X and added to it.  In the low-rank form,
 // with down weights A [r, K], up weights B [N, r] and a scalar scale:
-//   U = X A^T                  (lora_down_kernel; U kept as bfloat16 [M, r])
-//   Y[m, n] += scale * U B^T   (lora_up_add_kernel, on the convrot output Y)
+//   U = bf16(scale * X A^T)    (lora_down_kernel; bfloat16 [M, r])
+//   Y[m, n] += U B^T           (lora_up_add_kernel, on the convrot output Y;
+//                               the GEMM can also add it in its epilogue)
 // Both are small dense contractions on the bf16 matrix cores
 // (v_mfma_f32_32x32x16_bf16, float32 accumulation).  Operands go straight
 // from global memory (mostly L2: A, B and U are small) into the MFMA
@@ -58,7 +59,8 @@ template <typename InT, int NB>
 __global__ __launch_bounds__(256) void lora_down_kernel(const InT* __restrict__ x, int64_t ldx,
                                                         int m, int k,
                                                         const uint16_t* __restrict__ a, int r,
-                                                        uint16_t* __restrict__ u) {
+                                                        float scale, uint16_t* __restrict__ u,
+                                                        int64_t ldu) {
   __shared__ float part[4][NB][16][64];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row0 = blockIdx.x * 32;
@@ -86,25 +88,25 @@ __global__ __launch_bounds__(256) void lora_down_kernel(const InT* __restrict__ 
     for (int i = 0; i < 16; ++i) part[wave][b][i][lane] = acc[b][i];
   __syncthreads();
   // Wave w finishes column blocks w, w + 4, ...: sum the four partials in
-  // wave order, round to bfloat16, store.
+  // wave order, scale, round to bfloat16, store.
   for (int b = wave; b < NB; b += 4) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float v = ((part[0][b][i][lane] + part[1][b][i][lane]) + part[2][b][i][lane]) +
-                      part[3][b][i][lane];
+      const float v = scale * (((part[0][b][i][lane] + part[1][b][i][lane]) +
+                                part[2][b][i][lane]) + part[3][b][i][lane]);
       const int orow = row0 + 8 * (i / 4) + 4 * (lane >> 5) + (i & 3);
       const int ocol = b * 32 + lr;
-      if (orow < m && ocol < r) u[(int64_t)orow * r + ocol] = bf16_bits(v);
+      if (orow < m && ocol < r) u[(int64_t)orow * ldu + ocol] = bf16_bits(v);
     }
   }
 }
 
-// Y[128 x 128 tile] += scale * U B^T.  Each wave owns 64 x 64 (2 x 2 blocks of
+// Y[128 x 128 tile] += U B^T.  Each wave owns 64 x 64 (2 x 2 blocks of
 // 32 x 32); the rank r is the contraction length (steps of 16).  The tile's
 // Y values are read, updated and written back (float32).
 __global__ __launch_bounds__(256) void lora_up_add_kernel(const uint16_t* __restrict__ u,
                                                           const uint16_t* __restrict__ bw,
-                                                          int m, int n, int r, float scale,
+                                                          int64_t ldu, int m, int n, int r,
                                                           float* __restrict__ y, int64_t ldy) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tiles_n = (n + 127) / 128;
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(256) void lora_up_add_kernel(const uint16_t* __rest
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = m0 + i * 32 + lr;
-      ua[i] = as_bf16x8(load8(u + (int64_t)(row < m ? row : 0) * r + kk, row < m));
+      ua[i] = as_bf16x8(load8(u + (int64_t)(row < m ? row : 0) * ldu + kk, row < m));
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -156,27 +158,27 @@ __global__ __launch_bounds__(256) void lora_up_add_kernel(const uint16_t* __rest
         const int row = m0 + i * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e & 3);
         const int col = n0 + j * 32 + lr;
         if (row < m && col < n)
-          y[(int64_t)row * ldy + col] = __builtin_fmaf(scale, acc[i][j][e], yv[i][j][e]);
+          y[(int64_t)row * ldy + col] = yv[i][j][e] + acc[i][j][e];
       }
 }
 
 template <typename InT, int NB>
 hipError_t launch_down_t(const void* x, int64_t ldx, int m, int k, const uint16_t* a, int r,
-                         uint16_t* u, hipStream_t stream) {
+                         float scale, uint16_t* u, int64_t ldu, hipStream_t stream) {
   const int grid = (m + 31) / 32;
   hipLaunchKernelGGL((lora_down_kernel<InT, NB>), dim3(grid), dim3(256), 0, stream,
-                     static_cast<const InT*>(x), ldx, m, k, a, r, u);
+                     static_cast<const InT*>(x), ldx, m, k, a, r, scale, u, ldu);
   return hipGetLastError();
 }
 
 template <typename InT>
 hipError_t launch_down(const void* x, int64_t ldx, int m, int k, const uint16_t* a, int r,
-                       uint16_t* u, hipStream_t stream) {
+                       float scale, uint16_t* u, int64_t ldu, hipStream_t stream) {
   switch ((r + 31) / 32) {
-    case 1: return launch_down_t<InT, 1>(x, ldx, m, k, a, r, u, stream);
-    case 2: return launch_down_t<InT, 2>(x, ldx, m, k, a, r, u, stream);
-    case 3: return launch_down_t<InT, 3>(x, ldx, m, k, a, r, u, stream);
-    case 4: return launch_down_t<InT, 4>(x, ldx, m, k, a, r, u, stream);
+    case 1: return launch_down_t<InT, 1>(x, ldx, m, k, a, r, scale, u, ldu, stream);
+    case 2: return launch_down_t<InT, 2>(x, ldx, m, k, a, r, scale, u, ldu, stream);
+    case 3: return launch_down_t<InT, 3>(x, ldx, m, k, a, r, scale, u, ldu, stream);
+    case 4: return launch_down_t<InT, 4>(x, ldx, m, k, a, r, scale, u, ldu, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -185,17 +187,18 @@ static_assert(kLoraMaxBlocks == 4, "launch_down covers 1..4 column blocks");
 }  // namespace
 
 hipError_t launch_lora_down(const void* x, bool bf16, int64_t ldx, int64_t m, int64_t k,
-                            const uint16_t* a, int r, uint16_t* u, hipStream_t stream) {
-  return bf16 ? launch_down<uint16_t>(x, ldx, int(m), int(k), a, r, u, stream)
-              : launch_down<float>(x, ldx, int(m), int(k), a, r, u, stream);
+                            const uint16_t* a, int r, float scale, uint16_t* u, int64_t ldu,
+                            hipStream_t stream) {
+  return bf16 ? launch_down<uint16_t>(x, ldx, int(m), int(k), a, r, scale, u, ldu, stream)
+              : launch_down<float>(x, ldx, int(m), int(k), a, r, scale, u, ldu, stream);
 }
 
-hipError_t launch_lora_up_add(const uint16_t* u, const uint16_t* b, int64_t m, int64_t n, int r,
-                              float scale, float* y, int64_t ldy, hipStream_t stream) {
+hipError_t launch_lora_up_add(const uint16_t* u, int64_t ldu, const uint16_t* b, int64_t m,
+                              int64_t n, int r, float* y, int64_t ldy, hipStream_t stream) {
   const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
   if (tiles > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(lora_up_add_kernel, dim3(unsigned(tiles)), dim3(256), 0, stream, u, b, int(m), int(n), r,
-                     scale, y, ldy);
+  hipLaunchKernelGGL(lora_up_add_kernel, dim3(unsigned(tiles)), dim3(256), 0, stream, u, b, ldu,
+                     int(m), int(n), r, y, ldy);
   return hipGetLastError();
 }
 

@@ -180,37 +180,70 @@ convrot_status convrot_linear_grouped(const convrot_packed* x, const convrot_wei
  * base output and the adapter's correction, computed from the original
  * UNROTATED activation X, is added to it.  In the low-rank form, with down
  * weights A [rank, k], up weights B [n, rank] and a scale (alpha / rank):
- *   Y += scale * (X A^T) B^T.
- * Operands are bfloat16 with float32 accumulation; the rank-wide intermediate
- * U = X A^T is kept as bfloat16.  (The page gives no formula or precision for
- * the adapter path; this is the library's reading.)
- *
- * convrot_lora_down: U = X A^T.
+ *   U = bf16(scale * X A^T)          (convrot_lora_down)
+ *   Y += U B^T                       (fused: convrot_linear_lora;
+ *                                     separate: convrot_lora_up_add)
+ * Operands are bfloat16 with float32 accumulation; the scale is applied to
+ * the float32 sum X A^T, which is then rounded to bfloat16 (nearest even).
+ * (The page gives no formula or precision for the adapter path; this is the
+ * library's reading.)
+ */
+
+/*
+ * convrot_lora_down: U = bf16(scale * X A^T).
  *   x : device [m, k] of x_dtype (CONVROT_F32 or CONVROT_BF16), row stride
- *       ldx >= k; float32 X is rounded to bfloat16 (nearest even)
+ *       ldx >= k; float32 X is rounded to bfloat16 (nearest even) first
  *   a : device bfloat16 [rank, k], row stride k
- *   u : device bfloat16 [m, rank], row stride rank (output)
+ *   u : device bfloat16 [m, ldu] (output; columns rank .. ldu-1 untouched, so
+ *       several adapters' U can share one buffer)
  *   rank a multiple of 16 in 16 .. CONVROT_MAX_LORA_RANK; k % 16 == 0;
+ *   rank <= ldu <= 2^20 and ldu % 8 == 0;
  *   x, a, u 16-byte aligned, ldx in whole 16-byte units.
  * Errors: NULL, SHAPE, DTYPE, UNSUPPORTED, HIP.
  */
 convrot_status convrot_lora_down(const void* x, int32_t x_dtype, int64_t m, int64_t k,
-                                 int64_t ldx, const void* a, int32_t rank, void* u,
-                                 void* stream);
+                                 int64_t ldx, const void* a, int32_t rank, float scale, void* u,
+                                 int64_t ldu, void* stream);
 
 /*
- * convrot_lora_up_add: Y[i, o] += scale * sum_j U[i, j] B[o, j].
- *   u : device bfloat16 [m, rank] (from convrot_lora_down)
+ * convrot_lora_up_add: Y[i, o] += sum_j U[i, j] B[o, j], a separate pass over Y.
+ *   u : device bfloat16 [m, ldu] (from convrot_lora_down)
  *   b : device bfloat16 [n, rank], row stride rank
  *   y : device float32 [m, n], row stride ldy >= n (updated in place,
  *       typically the output of convrot_linear)
- *   rank as for convrot_lora_down; u and b 16-byte aligned, y 4-byte aligned;
- *   ceil(m / 128) * ceil(n / 128) <= INT32_MAX (128 x 128 output tiles).
+ *   rank and ldu as for convrot_lora_down; u and b 16-byte aligned, y 4-byte
+ *   aligned; ceil(m / 128) * ceil(n / 128) <= INT32_MAX (128 x 128 tiles).
  * Errors: NULL, SHAPE, UNSUPPORTED, HIP.
  */
-convrot_status convrot_lora_up_add(const void* u, const void* b, int64_t m, int64_t n,
-                                   int32_t rank, float scale, float* y, int64_t ldy,
-                                   void* stream);
+convrot_status convrot_lora_up_add(const void* u, int64_t ldu, const void* b, int64_t m,
+                                   int64_t n, int32_t rank, float* y, int64_t ldy, void* stream);
+
+/*
+ * One weight's adapter for convrot_linear_lora.
+ *   u    : device bfloat16 [m, ldu], this adapter's U from convrot_lora_down
+ *   b    : device bfloat16 [n, rank], row stride rank
+ *   ldu  : row stride of u in elements, rank <= ldu <= 2^20, ldu % 8 == 0
+ *   rank : a multiple of 16 in 16 .. CONVROT_MAX_LORA_RANK, or 0 for a weight
+ *          without an adapter (u, b and ldu are then ignored)
+ */
+typedef struct convrot_lora {
+  const void* u;
+  const void* b;
+  int64_t ldu;
+  int32_t rank;
+} convrot_lora;
+
+/*
+ * convrot_linear_grouped (float32 output) with each weight's adapter added
+ * in the GEMM epilogue, so Y is written once:
+ *   Y_i = act(A_i s_x s_w,i + b_i + U_i B_i^T)
+ * (act applies to the adapted output).  lora: host array of `count` adapters.
+ * Errors: those of convrot_linear_grouped; SHAPE or UNSUPPORTED for an
+ * adapter's rank, ldu or alignment; NULL for a missing u or b.
+ */
+convrot_status convrot_linear_lora(const convrot_packed* x, const convrot_weights* w,
+                                   const convrot_lora* lora, int32_t count, void* const* y,
+                                   const int64_t* ldy, int32_t act, void* stream);
 
 /* A static, human-readable name for a status code (never NULL). */
 const char* convrot_status_string(convrot_status status);

@@ -296,9 +296,9 @@ def reference_linear_fp64(x, w, bias=None) -> np.ndarray:
 # Readings (listed in the design doc as well): the device computes in bfloat16
 # operands with float32 accumulation, so the oracle takes the same operand
 # values -- X (bfloat16 as given, float32 inputs rounded to bfloat16), A and B
-# as bfloat16 values -- and, like the device, rounds the rank-r intermediate
-# U = X A^T to bfloat16 (round to nearest even) before the up projection.
-# All sums are float64.
+# as bfloat16 values.  The rank-r intermediate carries the scale and is
+# rounded to bfloat16 (nearest even): U = bf16(scale * X A^T); the
+# correction is then U B^T.  All sums are float64.
 
 
 def round_bf16(v: np.ndarray) -> np.ndarray:
@@ -313,21 +313,21 @@ def round_bf16(v: np.ndarray) -> np.ndarray:
     return np.ldexp(np.rint(np.ldexp(f, 8)), e - 8)
 
 
-def lora_down(x: np.ndarray, a: np.ndarray) -> np.ndarray:
-    """U = X A^T over the unrotated activation, rounded to bfloat16.
+def lora_down(x: np.ndarray, a: np.ndarray, scale: float) -> np.ndarray:
+    """U = scale * X A^T over the unrotated activation, rounded to bfloat16.
 
     x: [M, K] (values already bfloat16), a: [r, K] bfloat16 values.
     Returns float64 [M, r] holding bfloat16 values.
     """
     u = np.asarray(x, dtype=np.float64) @ np.asarray(a, dtype=np.float64).T
-    return round_bf16(u)
+    return round_bf16(float(scale) * u)
 
 
-def lora_up(u: np.ndarray, b: np.ndarray, scale: float) -> np.ndarray:
-    """The correction scale * U B^T (float64 [M, N]); b: [N, r]."""
-    return float(scale) * (np.asarray(u, dtype=np.float64) @ np.asarray(b, dtype=np.float64).T)
+def lora_up(u: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """The correction U B^T (float64 [M, N]); b: [N, r]."""
+    return np.asarray(u, dtype=np.float64) @ np.asarray(b, dtype=np.float64).T
 
 
 def lora_correction(x, a, b, scale) -> np.ndarray:
-    """scale * (X A^T) B^T with the bfloat16 intermediate (see above)."""
-    return lora_up(lora_down(x, a), b, scale)
+    """bf16(scale * X A^T) B^T (see above)."""
+    return lora_up(lora_down(x, a, scale), b)

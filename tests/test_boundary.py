@@ -192,12 +192,14 @@ def test_linear_grouped_validation():
     assert _grp(ws=empty, ys=[None, None], ldys=[0, 0]) == cr.OK   # nothing to launch
 
 
-def _down(x=FAKE, dt=cr.BF16, m=64, k=1024, ldx=None, a=FAKE, r=32, u=FAKE):
-    return cr.convrot_lora_down(x, dt, m, k, k if ldx is None else ldx, a, r, u)
+def _down(x=FAKE, dt=cr.BF16, m=64, k=1024, ldx=None, a=FAKE, r=32, u=FAKE, ldu=None):
+    return cr.convrot_lora_down(x, dt, m, k, k if ldx is None else ldx, a, r, 0.5, u,
+                                r if ldu is None else ldu)
 
 
-def _up(u=FAKE, b=FAKE, m=64, n=512, r=32, y=FAKE, ldy=None):
-    return cr.convrot_lora_up_add(u, b, m, n, r, 0.5, y, n if ldy is None else ldy)
+def _up(u=FAKE, b=FAKE, m=64, n=512, r=32, y=FAKE, ldy=None, ldu=None):
+    return cr.convrot_lora_up_add(u, r if ldu is None else ldu, b, m, n, r, y,
+                                  n if ldy is None else ldy)
 
 
 def test_lora_rank_limits_match_header():
@@ -207,16 +209,19 @@ def test_lora_rank_limits_match_header():
 
 @pytest.mark.parametrize("r", [0, 8, 15, 24, 136, 144, -16])
 def test_lora_rejects_bad_rank(r):
-    assert _down(r=r) == cr.ERR_SHAPE
-    assert _up(r=r) == cr.ERR_SHAPE
+    assert _down(r=r, ldu=max(r, 8)) == cr.ERR_SHAPE
+    assert _up(r=r, ldu=max(r, 8)) == cr.ERR_SHAPE
 
 
 def test_lora_down_validation():
     assert _down(k=0) == cr.ERR_SHAPE
     assert _down(m=-1) == cr.ERR_SHAPE
     assert _down(ldx=512) == cr.ERR_SHAPE           # ldx < k
+    assert _down(ldu=16) == cr.ERR_SHAPE            # ldu < rank
+    assert _down(ldu=(1 << 20) + 8) == cr.ERR_SHAPE
     assert _down(dt=2) == cr.ERR_DTYPE
     assert _down(k=1000) == cr.ERR_UNSUPPORTED       # k % 16
+    assert _down(ldu=36) == cr.ERR_UNSUPPORTED       # U rows not whole 16-byte units
     assert _down(x=None) == cr.ERR_NULL
     assert _down(a=None) == cr.ERR_NULL
     assert _down(u=None) == cr.ERR_NULL
@@ -229,6 +234,8 @@ def test_lora_down_validation():
 def test_lora_up_add_validation():
     assert _up(n=-1) == cr.ERR_SHAPE
     assert _up(ldy=100) == cr.ERR_SHAPE              # ldy < n
+    assert _up(ldu=16) == cr.ERR_SHAPE
+    assert _up(ldu=36) == cr.ERR_UNSUPPORTED
     assert _up(u=None) == cr.ERR_NULL
     assert _up(b=None) == cr.ERR_NULL
     assert _up(y=None) == cr.ERR_NULL
@@ -237,3 +244,47 @@ def test_lora_up_add_validation():
     assert _up(y=FAKE + 2) == cr.ERR_UNSUPPORTED
     assert _up(m=0, u=None, b=None, y=None) == cr.OK
     assert _up(n=0, u=None, b=None, y=None) == cr.OK
+
+
+def test_lora_struct_layout_matches_c():
+    # const void* u; const void* b; int64 ldu; int32 rank -> 28 bytes + padding
+    assert ctypes.sizeof(cr.ConvrotLora) == 32
+    assert cr.ConvrotLora.ldu.offset == 16 and cr.ConvrotLora.rank.offset == 24
+
+
+def _fused(loras=None, count=3, ws=None, act=cr.ACT_NONE, m=16, k=1024):
+    px = cr.ConvrotPacked(FAKE, FAKE, m, k, 256)
+    if ws is None:
+        ws = [cr.ConvrotWeights(FAKE, FAKE, None, 512, k, 256) for _ in range(count)]
+    if loras is None:
+        loras = [cr.ConvrotLora(FAKE, FAKE, 32, 32) for _ in ws]
+    return cr.convrot_linear_lora(px, ws, loras, [FAKE] * len(ws), [w.n for w in ws], act)
+
+
+def test_linear_lora_validation():
+    L = cr.lib()
+    assert L.convrot_linear_lora(None, None, None, 1, None, None, 0, None) == cr.ERR_NULL
+    px = cr.ConvrotPacked(FAKE, FAKE, 16, 1024, 256)
+    w1 = (cr.ConvrotWeights * 1)(cr.ConvrotWeights(FAKE, FAKE, None, 512, 1024, 256))
+    y1 = (ctypes.c_void_p * 1)(FAKE)
+    l1 = (ctypes.c_int64 * 1)(512)
+    assert L.convrot_linear_lora(ctypes.byref(px), w1, None, 1, y1, l1, 0, None) == cr.ERR_NULL
+    assert _fused(count=cr.MAX_GROUPED + 1) == cr.ERR_SHAPE
+    assert _fused(act=7) == cr.ERR_DTYPE
+    lo = lambda **kw: [cr.ConvrotLora(**{**dict(u=FAKE, b=FAKE, ldu=32, rank=32), **kw})] * 3
+    assert _fused(loras=lo(rank=24)) == cr.ERR_SHAPE
+    assert _fused(loras=lo(rank=144, ldu=144)) == cr.ERR_SHAPE
+    assert _fused(loras=lo(ldu=16)) == cr.ERR_SHAPE            # ldu < rank
+    assert _fused(loras=lo(ldu=36)) == cr.ERR_UNSUPPORTED
+    assert _fused(loras=lo(u=None)) == cr.ERR_NULL
+    assert _fused(loras=lo(b=None)) == cr.ERR_NULL
+    assert _fused(loras=lo(u=FAKE + 2)) == cr.ERR_UNSUPPORTED
+    assert _fused(loras=lo(b=FAKE + 8)) == cr.ERR_UNSUPPORTED
+    # rank 0: no adapter, pointers ignored -- validation passes through to the
+    # weights, where a bad ldy is the first error
+    none = [cr.ConvrotLora(None, None, 0, 0)] * 3
+    px = cr.ConvrotPacked(FAKE, FAKE, 16, 1024, 256)
+    ws = [cr.ConvrotWeights(FAKE, FAKE, None, 512, 1024, 256)] * 3
+    assert cr.convrot_linear_lora(px, ws, none, [FAKE] * 3, [512, 100, 512]) == cr.ERR_SHAPE
+    # empty m: nothing to launch, adapters unchecked beyond their shape
+    assert _fused(m=0, loras=lo(u=None, b=None)) == cr.OK

@@ -559,13 +559,14 @@ def test_linear_from_checkpoint(tmp_path):
 # ---------------------------------------------------------------------------
 # Low-rank adapter correction (bf16 operands, float32 accumulation)
 # ---------------------------------------------------------------------------
-# U is rounded to bf16 on both sides, but the device rounds a float32 sum and
+# U = bf16(scale X A^T) on both sides, but the device rounds a float32 sum and
 # the oracle a float64 one, so an element of U may sit one bf16 unit apart
 # where the sum lies next to a rounding boundary.  Bounds:
-#   U: |dU| <= 2^-8 |U_or| + float32 accumulation error (2^-24 k sum|x||a|),
-#      on at most 1% of elements;
-#   Y: |dY| <= scale (2^-8 |U_or| + eps_U) |B|^T + 2^-22 (|Y0| + scale |U||B|^T),
-#      and the correction's aggregate L1 error <= 1e-3 of its L1 norm.
+#   U: |dU| <= 2^-8 |U_or| + eps_U, eps_U = 2^-24 k |scale| sum|x||a| (float32
+#      accumulation), on at most 1% of elements;
+#   Y: |dY| <= (2^-8 |U_or| + eps_U) |B|^T + 2^-22 (|Y0| + |U||B|^T)
+#      (plus the convrot linear's own bound for a fused output), and the
+#      correction's aggregate L1 error <= 1e-3 of its L1 norm.
 LORA_U_MISMATCH_FRAC = 1e-2
 
 
@@ -578,25 +579,33 @@ def _lora_case(m, k, n, rank, x_dtype, seed):
     return inp["x"], x64, ad
 
 
-def _check_lora(u_dev, y_dev, x64, ad, what):
+def _lora_bounds(x64, ad):
+    """(U_or, eps_U, per-element bound on the correction, correction)."""
     a64, b64, scale = ad["a64"], ad["b64"], ad["scale"]
-    k = x64.shape[1]
-    u_or = orc.lora_down(x64, a64)
-    eps_u = 2.0**-24 * k * (np.abs(x64) @ np.abs(a64).T)
+    u_or = orc.lora_down(x64, a64, scale)
+    eps_u = 2.0**-24 * x64.shape[1] * abs(scale) * (np.abs(x64) @ np.abs(a64).T)
+    corr = orc.lora_up(u_or, b64)
+    mag = np.abs(u_or) @ np.abs(b64).T
+    bound = (2.0**-8 * np.abs(u_or) + eps_u) @ np.abs(b64).T + 2.0**-22 * mag
+    return u_or, eps_u, bound, corr
+
+
+def _check_u(u_dev, u_or, eps_u, what):
     du = np.abs(u_dev.astype(np.float64) - u_or)
     assert np.all(du <= 2.0**-8 * np.abs(u_or) + eps_u), f"{what}: U outside one bf16 unit"
     frac = np.count_nonzero(du) / max(1, du.size)
     assert frac <= LORA_U_MISMATCH_FRAC, f"{what}: {frac:.3%} of U differs"
-    corr = orc.lora_up(u_or, b64, scale)
+
+
+def _check_lora(u_dev, y_dev, x64, ad, what):
+    u_or, eps_u, bound, corr = _lora_bounds(x64, ad)
+    _check_u(u_dev, u_or, eps_u, what)
     y_or = ad["y0"].astype(np.float64) + corr
-    mag = scale * (np.abs(u_or) @ np.abs(b64).T)
-    bound = scale * ((2.0**-8 * np.abs(u_or) + eps_u) @ np.abs(b64).T) \
-        + 2.0**-22 * (np.abs(ad["y0"]) + mag)
+    bound = bound + 2.0**-22 * np.abs(ad["y0"])
     err = np.abs(y_dev.astype(np.float64) - y_or)
     assert np.all(err <= bound), f"{what}: Y bound exceeded by {np.max(err - bound):.3g}"
     rel = err.sum() / max(np.abs(corr).sum(), 1e-30)
     assert rel <= 1e-3, f"{what}: correction L1 error {rel:.3g}"
-    return frac, rel
 
 
 @pytest.mark.parametrize("m,k,n,rank,dt", [
@@ -607,13 +616,13 @@ def _check_lora(u_dev, y_dev, x64, ad, what):
 def test_lora_parity(m, k, n, rank, dt):
     x, x64, ad = _lora_case(m, k, n, rank, dt, seed=m + rank)
     _say(f"lora m={m} k={k} n={n} r={rank} {dt}")
-    u = cr.lora_down(dev(x), dev(ad["a"]))
+    u = cr.lora_down(dev(x), dev(ad["a"]), ad["scale"])
     y = dev(ad["y0"])
-    cr.lora_up_add(u, dev(ad["b"]), y, ad["scale"])
+    cr.lora_up_add(u, dev(ad["b"]), y)
     _check_lora(host(u.float()), host(y), x64, ad, f"lora {m}x{k}x{n} r{rank}")
 
 
-def test_lora_strided_x_and_y():
+def test_lora_strided_x_u_and_y():
     m, k, n, rank = 130, 1024, 300, 32
     x, x64, ad = _lora_case(m, k, n, rank, "bf16", seed=7)
     xs = torch.zeros((m, k + 64), dtype=torch.bfloat16)
@@ -622,16 +631,93 @@ def test_lora_strided_x_and_y():
     ys[:, :n] = torch.from_numpy(ad["y0"])
     _say("lora strided")
     xd, yd = xs.cuda(), ys.cuda()
-    u = cr.lora_down(xd[:, :k], dev(ad["a"]))
-    cr.lora_up_add(u, dev(ad["b"]), yd[:, :n], ad["scale"])
-    yh = host(yd)
+    ucat = torch.full((m, 3 * rank), 7.0, dtype=torch.bfloat16, device="cuda")
+    u = cr.lora_down(xd[:, :k], dev(ad["a"]), ad["scale"], out=ucat[:, rank:2 * rank])
+    cr.lora_up_add(u, dev(ad["b"]), yd[:, :n])
+    yh, uh = host(yd), host(ucat.float())
     assert np.all(yh[:, n:] == 3.0), "padding columns of Y were written"
-    _check_lora(host(u.float()), yh[:, :n], x64, ad, "lora strided")
+    assert np.all(uh[:, :rank] == 7.0) and np.all(uh[:, 2 * rank:] == 7.0), "U neighbours written"
+    _check_lora(uh[:, rank:2 * rank], yh[:, :n], x64, ad, "lora strided")
+
+
+def _fused_case(m, n_list, rank_list, k=3072, seed=21, gelu=False, g=256):
+    """Convrot linears on one pack with adapters fused into the epilogue,
+    against the oracle's linear plus correction."""
+    w = wl.Workload(name="fused", m=m, k=k, x_dtype="bf16", seed=seed,
+                    linears=tuple(wl.LinearSpec(f"w{i}", n, k) for i, n in enumerate(n_list)),
+                    channel_lognormal=True)
+    inp = wl.generate(w)
+    x = dev(inp["x"])
+    p = cr.pack_activations(x, g)
+    ws, adapters, ads = [], [], []
+    ucat_cols = sum(r for r in rank_list if r)
+    ucat = torch.empty((m, max(ucat_cols, 8)), dtype=torch.bfloat16, device="cuda")
+    col = 0
+    for i, (wt, b, r) in enumerate(zip(inp["weights"], inp["biases"], rank_list)):
+        ws.append(_prep(wt, b, g))
+        if not r:
+            adapters.append(None)
+            ads.append(None)
+            continue
+        ad = wl.lora_adapter(k, wt.shape[0], r, m=0, seed=seed + 10 * i)
+        u = cr.lora_down(x, dev(ad["a"]), ad["scale"], out=ucat[:, col:col + r])
+        col += r
+        adapters.append((u, dev(ad["b"])))
+        ads.append(ad)
+    ys = cr.linear_lora(p, ws, adapters, gelu=gelu)
+    qx_or, sx_or = orc.pack_activations(inp["x64"], g)
+    for i, (y, wt, b, ad) in enumerate(zip(ys, inp["weights"], inp["biases"], ads)):
+        qw_or, sw_or = orc.quantize_weights(wt, g)
+        pre = orc.linear(qx_or, sx_or, qw_or, sw_or, b)
+        bound = Y_ELEM * sx_or.astype(np.float64)[:, None] * sw_or.astype(np.float64)[None, :] * k * 127
+        if ad is not None:
+            u_or, eps_u, lb, corr = _lora_bounds(inp["x64"], ad)
+            pre = pre + corr
+            bound = bound + lb + 2.0**-22 * np.abs(pre)
+        y_or = orc.gelu(pre) if gelu else pre
+        if gelu:
+            bound = bound * GELU_LIPSCHITZ
+        err = np.abs(host(y).astype(np.float64) - y_or)
+        what = f"fused m={m} w{i} n={wt.shape[0]} r={rank_list[i]}{' gelu' if gelu else ''}"
+        assert np.all(err <= bound), f"{what}: bound exceeded by {np.max(err - bound):.3g}"
+        assert err.sum() / np.abs(y_or).sum() <= Y_MEAN_REL, what
+    return ys
+
+
+@pytest.mark.parametrize("m,ns,ranks", [
+    (320, (1000, 700, 512), (64, 0, 16)),     # edge tiles, one weight without an adapter
+    (512, (3072, 3072, 3072), (32, 48, 128)),  # interior tiles, every rank batch shape
+    (1100, (9000,), (64,)),                    # several tiles per workgroup
+])
+def test_linear_lora_fused(m, ns, ranks):
+    _say(f"fused lora m={m} n={ns} r={ranks}")
+    _fused_case(m, ns, ranks)
+
+
+def test_linear_lora_fused_gelu_and_short_k():
+    _say("fused lora gelu, k=512")
+    _fused_case(300, (1300,), (64,), k=512, gelu=True)
+    _say("fused lora gelu, k=3072")
+    _fused_case(600, (2000,), (32,), gelu=True)
+
+
+def test_linear_lora_rank_zero_matches_plain_linear():
+    """With no adapter the fused path's values equal the plain linear's bit for bit
+    (the same float32 expression A s_x s_w + b, evaluated at the tile end)."""
+    inp = wl.generate(wl.QKV, m=300, n_limit=900)
+    g = 256
+    p = cr.pack_activations(dev(inp["x"]), g)
+    ws = [_prep(wt, b, g) for wt, b in zip(inp["weights"], inp["biases"])]
+    _say("fused lora rank 0")
+    y_plain = cr.linear_grouped(p, ws)
+    y_fused = cr.linear_lora(p, ws, [None] * len(ws))
+    for a, b in zip(y_plain, y_fused):
+        assert torch.equal(a, b)
 
 
 def test_lora_on_convrot_output():
-    """The adapter's correction added to the convrot linear's output: the
-    complete adapted layer against the oracle's linear plus correction."""
+    """The separate up-add pass on the convrot linear's output: the complete
+    adapted layer against the oracle's linear plus correction."""
     inp = wl.generate(wl.QKV, m=320, n_limit=1000)
     g, rank = 256, 64
     wt, b = inp["weights"][0], inp["biases"][0]
@@ -639,14 +725,14 @@ def test_lora_on_convrot_output():
     _say("lora on convrot output")
     x = dev(inp["x"])
     y = cr.linear(cr.pack_activations(x, g), _prep(wt, b, g))
-    cr.lora_up_add(cr.lora_down(x, dev(ad["a"])), dev(ad["b"]), y, ad["scale"])
+    cr.lora_up_add(cr.lora_down(x, dev(ad["a"]), ad["scale"]), dev(ad["b"]), y)
     qx_or, sx_or = orc.pack_activations(inp["x64"], g)
     qw_or, sw_or = orc.quantize_weights(wt, g)
     base = orc.linear(qx_or, sx_or, qw_or, sw_or, b)
-    corr = orc.lora_correction(inp["x64"], ad["a64"], ad["b64"], ad["scale"])
+    _, _, lb, corr = _lora_bounds(inp["x64"], ad)
     y_or = base + corr
-    bound = Y_ELEM * sx_or[:, None] * sw_or[None, :].astype(np.float64) * wl.QKV.k * 127 \
-        + 2.0**-7 * ad["scale"] * (np.abs(orc.lora_down(inp["x64"], ad["a64"])) @ np.abs(ad["b64"]).T)
+    bound = Y_ELEM * sx_or[:, None] * sw_or[None, :].astype(np.float64) * wl.QKV.k * 127 + lb \
+        + 2.0**-22 * np.abs(y_or)
     err = np.abs(host(y).astype(np.float64) - y_or)
     assert np.all(err <= bound), f"adapted layer: bound exceeded by {np.max(err - bound):.3g}"
     assert err.sum() / np.abs(y_or).sum() <= Y_MEAN_REL
@@ -654,8 +740,8 @@ def test_lora_on_convrot_output():
 
 def test_lora_empty():
     a = torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda")
-    u = cr.lora_down(torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda"), a)
+    u = cr.lora_down(torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda"), a, 1.0)
     assert u.shape == (0, 16)
     y = torch.zeros((0, 8), device="cuda")
-    cr.lora_up_add(u, torch.zeros((8, 16), dtype=torch.bfloat16, device="cuda"), y, 1.0)
+    cr.lora_up_add(u, torch.zeros((8, 16), dtype=torch.bfloat16, device="cuda"), y)
     torch.cuda.synchronize()

@@ -414,7 +414,7 @@ def test_round_bf16_matches_torch_conversion():
 
 def test_lora_rank_one_closed_form():
     """A = e_j (one down row selecting feature j), B = ones: the correction is
-    scale * bf16(X[:, j]) in every output column."""
+    scale * X[:, j] in every output column (exact: scale is a power of two)."""
     rng = np.random.default_rng(12)
     x = orc.round_bf16(rng.standard_normal((5, 64)))
     a = np.zeros((1, 64))
@@ -424,9 +424,22 @@ def test_lora_rank_one_closed_form():
     assert np.array_equal(corr, np.repeat(0.5 * x[:, 17:18], 7, axis=1))
 
 
+def test_lora_scale_applies_before_the_bf16_rounding():
+    """x = 1 + 2^-7 (a bfloat16 value), scale 3: 3 x = 3.0234375 lies halfway
+    between the bfloat16 neighbours 3.015625 and 3.03125 and rounds to the even
+    one, 3.03125; scaling after the rounding would give 3.0234375."""
+    x = np.full((1, 16), 0.0)
+    x[0, 3] = 1.0 + 2.0**-7
+    a = np.zeros((1, 16))
+    a[0, 3] = 1.0
+    u = orc.lora_down(x, a, 3.0)
+    assert u[0, 0] == 3.03125
+    assert orc.lora_correction(x, a, np.array([[2.0]]), 3.0)[0, 0] == 6.0625
+
+
 def test_lora_equals_merged_weight_update():
-    """scale (X A^T) B^T equals X (scale B A)^T (the merged low-rank weight)
-    up to the bfloat16 rounding of the intermediate X A^T."""
+    """bf16(scale X A^T) B^T equals X (scale B A)^T (the merged low-rank
+    weight) up to the bfloat16 rounding of the intermediate."""
     rng = np.random.default_rng(13)
     x = orc.round_bf16(rng.standard_normal((9, 128)))
     a = orc.round_bf16(rng.standard_normal((16, 128)) * 0.05)
@@ -434,8 +447,8 @@ def test_lora_equals_merged_weight_update():
     scale = 2.0
     corr = orc.lora_correction(x, a, b, scale)
     merged = x @ (scale * b @ a).T
-    u_exact = x @ a.T
-    bound = scale * (np.abs(u_exact) * 2.0 ** -8) @ np.abs(b).T  # half-ulp per U element
+    u_exact = scale * (x @ a.T)
+    bound = (np.abs(u_exact) * 2.0 ** -8) @ np.abs(b).T  # half-ulp per U element
     assert np.all(np.abs(corr - merged) <= bound + 1e-12)
     assert not np.allclose(orc.lora_correction(x, a, b, -scale), merged)  # sign matters
     # transposed operands would not even have matching shapes
