@@ -181,8 +181,8 @@ convrot_status convrot_pack_activations(const void* x, int32_t x_dtype, int64_t 
 convrot_status convrot_lora_down(const void* x, int32_t x_dtype, int64_t m, int64_t k,
                                  int64_t ldx, const void* a, int32_t rank, float scale, void* u,
                                  int64_t ldu, void* stream) {
-  if (k < 1 || k > kMaxRows || m < 0 || m > kMaxRows || ldx < k || !lora_rank_ok(rank) ||
-      ldu < rank || ldu > convrot::kLoraMaxLdu)
+  if (k < 1 || m < 0 || m > kMaxRows || ldx < k || ldx > convrot::kLoraMaxLdx ||
+      !lora_rank_ok(rank) || ldu < rank || ldu > convrot::kLoraMaxLdu)
     return CONVROT_ERR_SHAPE;
   if (x_dtype != CONVROT_F32 && x_dtype != CONVROT_BF16) return CONVROT_ERR_DTYPE;
   if (k % 16 != 0 || ldu % 8 != 0) return CONVROT_ERR_UNSUPPORTED;

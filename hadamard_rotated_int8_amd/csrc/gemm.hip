@@ -14,12 +14,14 @@
 //     128 x BN/2 block of v_mfma_i32_32x32x32_i8 accumulators.  When a tile
 //     is complete its accumulators are copied into a second register set and
 //     the next tile starts from zero.
-//   * The finished tile is scaled and stored during the first 16 K steps of
-//     the next tile, two fixed groups of 2 x FN values per step, one store
-//     under each odd MFMA of the middle sub-steps.  Those 16 steps are
-//     unrolled, so every store names its registers at compile time and the
-//     K loop carries no store bookkeeping.  Output writes are thus spread over
-//     the main loop instead of bursting at tile ends.
+//   * The finished tile is stored during the first 8 K steps of the next
+//     tile (scaled on the way in the plain float32 mode; in the GELU and
+//     adapter modes it was made float32 at its end), 4 fixed groups of
+//     2 x FN values per step, one store under every other MFMA of the middle
+//     sub-steps.  Those 8 steps are unrolled, so every store names its
+//     registers at compile time and the K loop carries no store bookkeeping.
+//     Output writes are thus spread over the main loop instead of bursting
+//     at tile ends.
 //   * K advances 128 bytes per step (four 32-wide sub-steps).  Operands
 //     reach LDS by direct-to-LDS buffer loads of whole 128-byte lines, one
 //     per operand row and step, through two rings: Q_x in 2 stages (loaded
@@ -88,7 +90,12 @@ constexpr int kVmMax = 63;     // largest vmcnt a wait can name
 constexpr int kBufferWord3 = 0x00020000;
 constexpr unsigned kOutOfRange = 0x80000000u;  // an offset past every resource
 
-enum { kModeF32 = 0, kModeGelu = 1, kModeI32 = 2, kModeLora = 3, kModeLoraGelu = 4 };
+// Output modes.  kModeF32 scales each value as it is stored; the tile-end
+// modes turn the whole tile into float32 values at its end (and add the
+// adapters there), and only store them -- with GELU as well, which then
+// leaves the store-time VALU work to the erf alone (measurably faster than
+// scaling at store time too).
+enum { kModeF32 = 0, kModeI32 = 2, kModeTileEnd = 3, kModeTileEndGelu = 4 };
 
 template <int BN>
 struct Cfg {
@@ -237,11 +244,11 @@ template <int BN, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p) {
   using C = Cfg<BN>;
   constexpr int FM = C::FM, FN = C::FN, NV = C::NV, NG = C::NG, NSS = C::NSS;
-  constexpr bool LORA = MODE == kModeLora || MODE == kModeLoraGelu;
-  constexpr bool GELU = MODE == kModeGelu || MODE == kModeLoraGelu;
+  constexpr bool LORA = MODE == kModeTileEnd || MODE == kModeTileEndGelu;  // tile-end epilogue
+  constexpr bool GELU = MODE == kModeTileEndGelu;
   // Scales and bias applied when a value is stored (otherwise the pending
   // values are raw int32 results or finished float32 values).
-  constexpr bool SCALE_AT_STORE = MODE == kModeF32 || MODE == kModeGelu;
+  constexpr bool SCALE_AT_STORE = MODE == kModeF32;
   __shared__ __attribute__((aligned(1024))) int8_t smem[C::LDS];
 
   const int lane = threadIdx.x & 63;
@@ -645,9 +652,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
   // (A s_x s_w + b, from the tile's parameter buffer, the rounding of the
   // store-time path), and U B^T is accumulated onto them.  U and B fragments
   // come straight from global memory (L2) by buffer loads whose resources
-  // span the tile's valid rows, so rows past M or n read as zero; two 16-wide
-  // rank slices are requested at a time, then their MFMAs run.
+  // span the tile's valid rows, so rows past M or n read as zero.  The rank
+  // is walked in 16-wide slices (unrolled: rank <= kLoraMaxRank), each
+  // requested one slice ahead (deeper prefetch spills in the K loop); the
+  // first is requested before the float32 conversion, whose VALU work covers
+  // its latency.  These are loads into registers, so the compiler's own
+  // waits cover them.
   auto lora_epilogue = [&](int t_it) __attribute__((always_inline)) {
+    constexpr int NSL = kLoraMaxRank / 16, PF = 1;
     reload_uniforms();
     // Lane-derived offsets are formed here, from a copy the compiler cannot
     // see through, rather than hoisted out of the tile loop (live across
@@ -658,6 +670,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
     const Seg& sg = p.seg[ti.s];
     const int8_t* par = smem + C::PAR0 + (t_it & 1) * C::PARB;
     const int wm = wave >> 1, wn = wave & 1;
+    const int rank = sg.rank;  // 0 or a multiple of 16
+    const int rows = M - ti.m0 < kBM ? M - ti.m0 : kBM;
+    const int cols = sg.n - ti.n0 < BN ? sg.n - ti.n0 : BN;
+    const int ldu = sg.ldu;
+    const __amdgpu_buffer_rsrc_t ur = buffer_rsrc(sg.lu + (int64_t)ti.m0 * ldu, rows * ldu * 2);
+    const __amdgpu_buffer_rsrc_t br = buffer_rsrc(sg.lb + (int64_t)ti.n0 * rank, cols * rank * 2);
+    // Lane l: row l % 32 of a 32-row block, bf16 elements 8 (l / 32) .. +7
+    // of a 16-wide rank slice (both operands; the sum runs over all 16).
+    const unsigned uoff = unsigned(((wm * 128 + (lane & 31)) * ldu + 8 * (lane >> 5)) * 2);
+    const unsigned boff = unsigned(((wn * C::WN + (lane & 31)) * rank + 8 * (lane >> 5)) * 2);
+    v4i uf[NSL][FM], bfr[NSL][FN];
+    auto load_slice = [&](int sl) {
+      if (16 * sl < rank) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          uf[sl][i] = __builtin_bit_cast(
+              v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                       ur, uoff + unsigned((i * 32 * ldu + 16 * sl) * 2), 0, 0));
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          bfr[sl][j] = __builtin_bit_cast(
+              v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                       br, boff + unsigned((j * 32 * rank + 16 * sl) * 2), 0, 0));
+      }
+    };
+#pragma unroll
+    for (int sl = 0; sl < PF; ++sl) load_slice(sl);
+
     const bool has_b = sg.bias != nullptr;
     float sw[FN], bb[FN];
 #pragma unroll
@@ -683,50 +723,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
             acc[i][j][e] = __float_as_int(__builtin_fmaf((float)acc[i][j][e] * sx4[rr], sw[j], bb[j]));
           }
       }
-    const int rank = sg.rank;
-    if (rank > 0) {
-      const int rows = M - ti.m0 < kBM ? M - ti.m0 : kBM;
-      const int cols = sg.n - ti.n0 < BN ? sg.n - ti.n0 : BN;
-      const int ldu = sg.ldu;
-      const __amdgpu_buffer_rsrc_t ur = buffer_rsrc(sg.lu + (int64_t)ti.m0 * ldu, rows * ldu * 2);
-      const __amdgpu_buffer_rsrc_t br = buffer_rsrc(sg.lb + (int64_t)ti.n0 * rank, cols * rank * 2);
-      // Lane l: row l % 32 of a 32-row block, bf16 elements 8 (l / 32) .. +7
-      // of a 16-wide rank slice (both operands; the sum runs over all 16).
-      const unsigned uoff = unsigned(((wm * 128 + (lane & 31)) * ldu + 8 * (lane >> 5)) * 2);
-      const unsigned boff = unsigned(((wn * C::WN + (lane & 31)) * rank + 8 * (lane >> 5)) * 2);
-      constexpr int KS = 2;  // 16-wide rank slices per batch of loads
-      for (int k0 = 0; k0 < rank; k0 += 16 * KS) {
-        v4i uf[KS][FM], bfr[KS][FN];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          if (k0 + 16 * ks < rank) {
+    for (int sl = 0; sl < NSL; ++sl) {
+      if (16 * sl < rank) {
+        if (sl + PF < NSL) load_slice(sl + PF);
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-              uf[ks][i] = __builtin_bit_cast(
-                  v4i, __builtin_amdgcn_raw_buffer_load_b128(
-                           ur, uoff + unsigned((i * 32 * ldu + k0 + 16 * ks) * 2), 0, 0));
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-              bfr[ks][j] = __builtin_bit_cast(
-                  v4i, __builtin_amdgcn_raw_buffer_load_b128(
-                           br, boff + unsigned((j * 32 * rank + k0 + 16 * ks) * 2), 0, 0));
-          }
-        }
-        waitvm_c<0>();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          if (k0 + 16 * ks < rank) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-              for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_bit_cast(
-                    v16i, __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                              __builtin_bit_cast(bf16x8, uf[ks][i]),
-                              __builtin_bit_cast(bf16x8, bfr[ks][j]),
-                              __builtin_bit_cast(f32x16, acc[i][j]), 0, 0, 0));
-          }
-        }
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_bit_cast(
+                v16i, __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                          __builtin_bit_cast(bf16x8, uf[sl][i]),
+                          __builtin_bit_cast(bf16x8, bfr[sl][j]),
+                          __builtin_bit_cast(f32x16, acc[i][j]), 0, 0, 0));
       }
     }
   };
@@ -879,13 +888,12 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     s.ldu = int(a.w[i].ldu);
     s.rank = a.lora ? a.w[i].rank : 0;
   }
-  if (a.lora) {
-    if (a.raw_i32) return hipErrorInvalidValue;
-    if (a.gelu) return launch_t<kBN, kModeLoraGelu>(p, stream);
-    return launch_t<kBN, kModeLora>(p, stream);
+  if (a.raw_i32) {
+    if (a.lora || a.gelu) return hipErrorInvalidValue;
+    return launch_t<kBN, kModeI32>(p, stream);
   }
-  if (a.raw_i32) return launch_t<kBN, kModeI32>(p, stream);
-  if (a.gelu) return launch_t<kBN, kModeGelu>(p, stream);
+  if (a.gelu) return launch_t<kBN, kModeTileEndGelu>(p, stream);  // ranks 0 without adapters
+  if (a.lora) return launch_t<kBN, kModeTileEnd>(p, stream);
   return launch_t<kBN, kModeF32>(p, stream);
 }
 

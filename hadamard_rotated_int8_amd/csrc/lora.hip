@@ -10,9 +10,10 @@
 //                               the GEMM can also add it in its epilogue)
 // Both are small dense contractions on the bf16 matrix cores
 // (v_mfma_f32_32x32x16_bf16, float32 accumulation).  Operands go straight
-// from global memory (mostly L2: A, B and U are small) into the MFMA
-// register layout -- each lane reads 16 contiguous bytes of one row -- so no
-// LDS staging is needed for the operands.
+// from global memory into the MFMA register layout; no LDS staging.  The
+// down projection streams X once from HBM (A is small and stays in L2).
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -23,12 +24,23 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kLoraMaxBlocks = kLoraMaxRank / 32;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 
-// float32 -> bfloat16 bits, round to nearest even (finite inputs).
+// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format).
+constexpr int kBufferWord3 = 0x00020000;
+constexpr unsigned kOutOfRange = 0x80000000u;  // an offset past every resource
+
+CR_DEVICE __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes,
+                                           kBufferWord3);
+}
+
+// float32 -> bfloat16 bits, round to nearest even (v_cvt_pk_bf16_f32).
 CR_DEVICE unsigned short bf16_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (unsigned short)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+  const bf16x2 r = __builtin_convertvector(f32x2{f, 0.f}, bf16x2);
+  return __builtin_bit_cast(unsigned short, r.x);
 }
 
 CR_DEVICE bf16x8 as_bf16x8(u16x8 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -39,65 +51,182 @@ CR_DEVICE u16x8 load8(const uint16_t* __restrict__ p, bool ok) {
   if (!ok) return u16x8{};
   return __builtin_bit_cast(u16x8, *reinterpret_cast<const u32x4*>(p));
 }
-CR_DEVICE u16x8 load8(const float* __restrict__ p, bool ok) {
-  u16x8 r{};
-  if (!ok) return r;
-  const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
-  const f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
-  r[0] = bf16_bits(a.x); r[1] = bf16_bits(a.y); r[2] = bf16_bits(a.z); r[3] = bf16_bits(a.w);
-  r[4] = bf16_bits(b.x); r[5] = bf16_bits(b.y); r[6] = bf16_bits(b.z); r[7] = bf16_bits(b.w);
-  return r;
+
+// Position of workgroup b in a grid of n: workgroups go to the 8 XCDs round
+// robin, and each XCD takes a contiguous run of positions.
+CR_DEVICE int xcd_slot(int b, int n) {
+  const int xcd = b % 8, idx = b / 8;
+  const int q = n / 8, rem = n % 8;
+  return (xcd < rem) ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
 }
 
-// U[32-row block] = X A^T.  A workgroup of 4 waves owns 32 rows; the 16-wide
-// K steps are dealt round robin over the waves, and the four partial sums
-// are added in LDS in wave order (deterministic).  NB = ceil(r / 32) column
-// blocks of U.  MFMA operand layout: lane l holds row l % 32, features
-// 8 (l / 32) .. 8 (l / 32) + 7 of the step; accumulator register i of lane l
-// is row 8 (i / 4) + 4 (l / 32) + i % 4, column l % 32.
-template <typename InT, int NB>
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt vmcnt(N), other counters unchanged (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+template <int N>
+CR_DEVICE void waitvm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+CR_DEVICE void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// f(integral_constant<int, I>) for every I of the sequence, in order.
+template <int... I, typename F>
+CR_DEVICE void for_each_index(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+
+// U[32 x 32 block] = bf16(scale * X A^T).  The workgroup's 4 waves share the
+// 64-wide K blocks round robin and add their partial sums in LDS in wave
+// order (deterministic).  Blocks are numbered column block fastest and dealt
+// XCD by XCD, so the column blocks of one row block read X through one L2.
+//
+// Each wave streams its K blocks through a private ring of D LDS stages by
+// direct-to-LDS buffer loads: 16 bytes per lane with consecutive lanes on
+// consecutive 16-byte chunks of a row, so every instruction reads whole
+// 128-byte lines.  The resources span the block's valid rows and features
+// past k are given an out-of-range offset, so both read as zero.  Chunk c
+// of stage row r sits at slot c ^ swz(r), which spreads the 16 rows a
+// quarter-wave reads over all LDS banks.
+//
+// MFMA operands: for K block kb, lane l (row l % 32 of the block, h = l / 32)
+// takes features 32h + 8c .. +7 of the block in MFMA c (c = 0..3); X and A use
+// the same assignment, so the four MFMAs sum over all 64 features.
+// Accumulator register i of lane l is row 8 (i / 4) + 4 (l / 32) + i % 4,
+// column l % 32 of the 32 x 32 block.
+template <typename InT, int D>
 __global__ __launch_bounds__(256) void lora_down_kernel(const InT* __restrict__ x, int64_t ldx,
                                                         int m, int k,
                                                         const uint16_t* __restrict__ a, int r,
                                                         float scale, uint16_t* __restrict__ u,
-                                                        int64_t ldu) {
-  __shared__ float part[4][NB][16][64];
+                                                        int64_t ldu, int ncb) {
+  constexpr int ES = sizeof(InT);
+  constexpr int XROW = 64 * ES;           // bytes of X per row and K block
+  constexpr int XCH = XROW / 16;          // 16-byte chunks per X row (8 or 16)
+  constexpr int XST = 32 * XROW;          // X bytes per stage
+  constexpr int STAGE = XST + 32 * 128;   // + A (32 rows x 128 bytes)
+  constexpr int XL = XST / 1024, AL = 4;  // load instructions per stage
+  constexpr int LPB = XL + AL;
+  static_assert((D - 1) * LPB <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) int8_t smem[4 * D * STAGE];
+  static_assert(4 * D * STAGE >= 4 * 16 * 64 * 4, "the reduction reuses the stages");
+
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int row0 = blockIdx.x * 32;
-  const int lr = lane & 31, kh = (lane >> 5) * 8;
-  const int row = row0 + lr;
-  const InT* xr = x + (int64_t)(row < m ? row : 0) * ldx;
-  f32x16 acc[NB];
+  const int nrb = (m + 31) / 32;
+  const int pos = xcd_slot(blockIdx.x, nrb * ncb);
+  const int row0 = (pos / ncb) * 32, col0 = (pos % ncb) * 32;
+  const int rows = m - row0 < 32 ? m - row0 : 32;
+  const int cols = r - col0 < 32 ? r - col0 : 32;
+  const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x + (int64_t)row0 * ldx, int(rows * ldx * ES));
+  const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(a + (int64_t)col0 * k, cols * k * 2);
+  const int nkb = (k + 63) / 64;
+  const int T = nkb > wave ? (nkb - wave + 3) / 4 : 0;  // this wave's K blocks: wave + 4t
+  int8_t* ring = smem + wave * D * STAGE;
+
+  // X rows: lane j of load instruction q fills stage row q*(64/XCH) + j/XCH,
+  // slot j%XCH, with global chunk slot ^ swz(row).  Same for A (8 chunks).
+  auto xswz = [](int row) { return XCH == 8 ? (row >> 1) & 7 : row & 15; };
+  auto aswz = [](int row) { return (row >> 1) & 7; };
+  auto issue = [&](int st, int t) {
+    const int f0 = (wave + 4 * t) * 64;  // first feature of the K block
+    int8_t* xs = ring + st * STAGE;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = f32x16{};
-  const int nsteps = (k + 15) / 16;
-  for (int s = wave; s < nsteps; s += 4) {
-    const int kk = s * 16 + kh;
-    const bool kok = kk < k;  // k is a multiple of 16, so a lane's 8 features are all in or all out
-    const bf16x8 xa = as_bf16x8(load8(xr + kk, kok && row < m));
+    for (int q = 0; q < XL; ++q) {
+      const int row = q * (64 / XCH) + lane / XCH;
+      const int ch = (lane % XCH) ^ xswz(row);
+      const int f = f0 + ch * (16 / ES);
+      const unsigned off = f < k ? unsigned(row * ldx * ES + f * ES) : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void*)(xs + q * 1024), 16, off, 0, 0, 0);
+    }
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int ar = b * 32 + lr;
-      const bf16x8 ab = as_bf16x8(load8(a + (int64_t)(ar < r ? ar : 0) * k + kk, kok && ar < r));
-      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, ab, acc[b], 0, 0, 0);
+    for (int q = 0; q < AL; ++q) {
+      const int row = q * 8 + lane / 8;
+      const int ch = (lane % 8) ^ aswz(row);
+      const int f = f0 + ch * 8;
+      const unsigned off = f < k ? unsigned(row * k * 2 + f * 2) : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void*)(xs + XST + q * 1024), 16, off, 0,
+                                               0, 0);
+    }
+  };
+  const int lr = lane & 31, h = lane >> 5;
+  auto x_operand = [&](const int8_t* xs, int c) -> bf16x8 {
+    if constexpr (ES == 2) {
+      const int ch = (4 * h + c) ^ xswz(lr);
+      return *reinterpret_cast<const bf16x8*>(xs + lr * XROW + ch * 16);
+    } else {
+      const int c0 = (8 * h + 2 * c) ^ xswz(lr), c1 = (8 * h + 2 * c + 1) ^ xswz(lr);
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(xs + lr * XROW + c0 * 16);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(xs + lr * XROW + c1 * 16);
+      const bf16x2 p0 = __builtin_convertvector(f32x2{lo.x, lo.y}, bf16x2);
+      const bf16x2 p1 = __builtin_convertvector(f32x2{lo.z, lo.w}, bf16x2);
+      const bf16x2 p2 = __builtin_convertvector(f32x2{hi.x, hi.y}, bf16x2);
+      const bf16x2 p3 = __builtin_convertvector(f32x2{hi.z, hi.w}, bf16x2);
+      return bf16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+    }
+  };
+  auto a_operand = [&](const int8_t* as, int c) -> bf16x8 {
+    const int ch = (4 * h + c) ^ aswz(lr);
+    return *reinterpret_cast<const bf16x8*>(as + lr * 128 + ch * 16);
+  };
+
+  f32x16 acc = {};
+  auto consume = [&](int st) {
+    const int8_t* xs = ring + st * STAGE;
+    bf16x8 xo[4], ao[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      xo[c] = x_operand(xs, c);
+      ao[c] = a_operand(xs + XST, c);
+    }
+    wait_lgkm0();
+    return [=, &acc]() {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xo[c], ao[c], acc, 0, 0, 0);
+    };
+  };
+#pragma unroll
+  for (int st = 0; st < D; ++st) issue(st, st);
+  // Rounds of D blocks; blocks past the wave's last one read as zero.  For
+  // each stage: wait until only the later stages' loads are in flight, read
+  // the fragments, and once they are in registers refill the stage D blocks
+  // ahead.  The last round refills nothing, so its waits count down.
+  const int rounds = (T + D - 1) / D;
+  for (int rd = 0; rd + 1 < rounds; ++rd) {
+#pragma unroll
+    for (int st = 0; st < D; ++st) {
+      waitvm<(D - 1) * LPB>();
+      auto mfmas = consume(st);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(st, rd * D + st + D);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas();
     }
   }
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) part[wave][b][i][lane] = acc[b][i];
+  if (rounds > 0) {
+    for_each_index(std::make_integer_sequence<int, D>{}, [&](auto stc) {
+      constexpr int st = decltype(stc)::value;
+      waitvm<(D - 1 - st) * LPB>();
+      consume(st)();
+    });
+  }
+  waitvm<0>();  // (a wave without blocks still has its first stages in flight)
   __syncthreads();
-  // Wave w finishes column blocks w, w + 4, ...: sum the four partials in
-  // wave order, scale, round to bfloat16, store.
-  for (int b = wave; b < NB; b += 4) {
+  float* part = reinterpret_cast<float*>(smem);  // [4][16][64]
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float v = scale * (((part[0][b][i][lane] + part[1][b][i][lane]) +
-                                part[2][b][i][lane]) + part[3][b][i][lane]);
-      const int orow = row0 + 8 * (i / 4) + 4 * (lane >> 5) + (i & 3);
-      const int ocol = b * 32 + lr;
-      if (orow < m && ocol < r) u[(int64_t)orow * ldu + ocol] = bf16_bits(v);
-    }
+  for (int i = 0; i < 16; ++i) part[(wave * 16 + i) * 64 + lane] = acc[i];
+  __syncthreads();
+  // Wave w finishes registers 4w .. 4w+3: the four partials in wave order,
+  // scaled, rounded to bfloat16.
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    const int i = 4 * wave + ii;
+    const float v = scale * (((part[i * 64 + lane] + part[(16 + i) * 64 + lane]) +
+                              part[(32 + i) * 64 + lane]) + part[(48 + i) * 64 + lane]);
+    const int orow = row0 + 8 * (i / 4) + 4 * h + (i & 3);
+    const int ocol = col0 + lr;
+    if (orow < m && ocol < r) u[(int64_t)orow * ldu + ocol] = bf16_bits(v);
   }
 }
 
@@ -162,27 +291,17 @@ __global__ __launch_bounds__(256) void lora_up_add_kernel(const uint16_t* __rest
       }
 }
 
-template <typename InT, int NB>
-hipError_t launch_down_t(const void* x, int64_t ldx, int m, int k, const uint16_t* a, int r,
-                         float scale, uint16_t* u, int64_t ldu, hipStream_t stream) {
-  const int grid = (m + 31) / 32;
-  hipLaunchKernelGGL((lora_down_kernel<InT, NB>), dim3(grid), dim3(256), 0, stream,
-                     static_cast<const InT*>(x), ldx, m, k, a, r, scale, u, ldu);
-  return hipGetLastError();
-}
-
 template <typename InT>
 hipError_t launch_down(const void* x, int64_t ldx, int m, int k, const uint16_t* a, int r,
                        float scale, uint16_t* u, int64_t ldu, hipStream_t stream) {
-  switch ((r + 31) / 32) {
-    case 1: return launch_down_t<InT, 1>(x, ldx, m, k, a, r, scale, u, ldu, stream);
-    case 2: return launch_down_t<InT, 2>(x, ldx, m, k, a, r, scale, u, ldu, stream);
-    case 3: return launch_down_t<InT, 3>(x, ldx, m, k, a, r, scale, u, ldu, stream);
-    case 4: return launch_down_t<InT, 4>(x, ldx, m, k, a, r, scale, u, ldu, stream);
-    default: return hipErrorInvalidValue;
-  }
+  const int ncb = (r + 31) / 32;
+  const int64_t blocks = int64_t((m + 31) / 32) * ncb;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  constexpr int D = sizeof(InT) == 2 ? 4 : 3;  // LDS stages per wave (128 KB / 144 KB)
+  hipLaunchKernelGGL((lora_down_kernel<InT, D>), dim3(unsigned(blocks)), dim3(256), 0, stream,
+                     static_cast<const InT*>(x), ldx, m, k, a, r, scale, u, ldu, ncb);
+  return hipGetLastError();
 }
-static_assert(kLoraMaxBlocks == 4, "launch_down covers 1..4 column blocks");
 
 }  // namespace
 
