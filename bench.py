@@ -177,6 +177,37 @@ def all_configs(args):
                 emit(workload=w.name, kernel="linear_grouped", n=n_total, m=m, k=k, group_size=g,
                      us=round(t * 1e3, 2), tops=round(tops, 1), mfma_frac=round(tops / PEAK_INT8_TOPS, 4))
                 del ys
+            # Rank-64 low-rank adapters on the workload's linears (the first,
+            # GELU one for the MLP): the down projection of each adapter into
+            # one shared U buffer, and the linears with U B^T added in the
+            # GEMM epilogue, beside the same launch without adapters.
+            if g == 256 and m >= 1024:
+                rank = 64
+                lqws = qws[:1] if w.gelu_chain else qws
+                ads = [wl.lora_adapter(k, q.q.shape[0], rank, m=0, seed=w.seed + 50 + i)
+                       for i, q in enumerate(lqws)]
+                a_dev = [ad["a"].cuda() for ad in ads]
+                b_dev = [ad["b"].cuda() for ad in ads]
+                ucat = torch.empty((m, rank * len(ads)), dtype=torch.bfloat16, device="cuda")
+                us = [ucat[:, i * rank:(i + 1) * rank] for i in range(len(ads))]
+
+                def down_all():
+                    for ad, a_d, u in zip(ads, a_dev, us):
+                        cr.lora_down(x, a_d, ad["scale"], out=u)
+
+                td = _time_ms(down_all)
+                emit(workload=w.name, kernel="lora_down", m=m, k=k, rank=rank, adapters=len(ads),
+                     us=round(td * 1e3, 2),
+                     x_gbps=round(len(ads) * m * k * xb / (td * 1e-3) / 1e9, 1))
+                ys = [torch.empty((m, q.q.shape[0]), dtype=torch.float32, device="cuda") for q in lqws]
+                gl = w.gelu_chain
+                t0 = _time_ms(lambda: cr.linear_lora(packed, lqws, [None] * len(lqws), outs=ys, gelu=gl))
+                tl = _time_ms(lambda: cr.linear_lora(packed, lqws, list(zip(us, b_dev)), outs=ys, gelu=gl))
+                n_total = sum(q.q.shape[0] for q in lqws)
+                emit(workload=w.name, kernel="linear_lora", m=m, n=n_total, k=k, rank=rank,
+                     gelu=gl, us_without_adapters=round(t0 * 1e3, 2), us=round(tl * 1e3, 2),
+                     adapter_overhead=round(tl / t0 - 1.0, 4))
+                del ys, ucat, us, a_dev, b_dev
             # The oracle on a row sample of the same workload (weights quantised
             # offline and untimed, as on the device).
             rows = min(m, 64)
