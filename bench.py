@@ -21,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -201,8 +202,15 @@ def all_configs(args):
                      x_gbps=round(len(ads) * m * k * xb / (td * 1e-3) / 1e9, 1))
                 ys = [torch.empty((m, q.q.shape[0]), dtype=torch.float32, device="cuda") for q in lqws]
                 gl = w.gelu_chain
-                t0 = _time_ms(lambda: cr.linear_lora(packed, lqws, [None] * len(lqws), outs=ys, gelu=gl))
-                tl = _time_ms(lambda: cr.linear_lora(packed, lqws, list(zip(us, b_dev)), outs=ys, gelu=gl))
+                # Alternate the two launches and take medians: the first
+                # rounds after a change of kernel run at a lower clock.
+                t0s, tls = [], []
+                for _ in range(6):
+                    t0s.append(_time_ms(lambda: cr.linear_lora(packed, lqws, [None] * len(lqws),
+                                                               outs=ys, gelu=gl)))
+                    tls.append(_time_ms(lambda: cr.linear_lora(packed, lqws, list(zip(us, b_dev)),
+                                                               outs=ys, gelu=gl)))
+                t0, tl = statistics.median(t0s), statistics.median(tls)
                 n_total = sum(q.q.shape[0] for q in lqws)
                 emit(workload=w.name, kernel="linear_lora", m=m, n=n_total, k=k, rank=rank,
                      gelu=gl, us_without_adapters=round(t0 * 1e3, 2), us=round(tl * 1e3, 2),

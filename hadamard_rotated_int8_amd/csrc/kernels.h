@@ -52,7 +52,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 
 constexpr int kLoraMaxRank = 128;        // adapter ranks 16, 32, ..., 128
 constexpr int64_t kLoraMaxLdu = 1 << 20;  // U row stride limit (32-bit buffer offsets)
-constexpr int64_t kLoraMaxLdx = 1 << 22;  // X row stride limit of the down projection (same)
+constexpr int64_t kLoraMaxLdx = 1 << 21;  // X row stride limit of the down projection (same)
 
 // U = bf16(scale X A^T) (bfloat16 [m, r], row stride ldu); X [m, k] bf16 or
 // float32, A bfloat16 [r, k].

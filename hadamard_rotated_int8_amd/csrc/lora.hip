@@ -71,6 +71,11 @@ CR_DEVICE void waitvm() {
 }
 CR_DEVICE void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// A bare s_barrier (the waits are explicit; a __syncthreads fence would also
+// drain the loads still in flight for later stages).  The memory clobber
+// keeps LDS accesses on their side of it.
+CR_DEVICE void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // f(integral_constant<int, I>) for every I of the sequence, in order.
 template <int... I, typename F>
 CR_DEVICE void for_each_index(std::integer_sequence<int, I...>, F&& f) {
@@ -230,6 +235,118 @@ __global__ __launch_bounds__(256) void lora_down_kernel(const InT* __restrict__ 
   }
 }
 
+// U[128 x 32 NB block] = bf16(scale * X A^T) for long X (many row blocks):
+// each wave owns 32 rows and all NB column blocks of U, so A is read once
+// per 128 rows and X once per row.  The 4 waves share a ring of D LDS
+// stages (X rows of the block and A rows, 64 features each), filled by
+// direct-to-LDS loads spread over the waves; one barrier per K block.
+// Operand assignment, swizzle and zero fill as in lora_down_kernel.
+template <typename InT, int NB, int D>
+__global__ __launch_bounds__(256) void lora_down_rows_kernel(const InT* __restrict__ x,
+                                                             int64_t ldx, int m, int k,
+                                                             const uint16_t* __restrict__ a,
+                                                             int r, float scale,
+                                                             uint16_t* __restrict__ u,
+                                                             int64_t ldu) {
+  constexpr int ES = sizeof(InT);
+  constexpr int XROW = 64 * ES;           // bytes of X per row and K block
+  constexpr int XCH = XROW / 16;          // 16-byte chunks per X row
+  constexpr int XST = 128 * XROW;         // X bytes per stage
+  constexpr int STAGE = XST + 32 * NB * 128;
+  constexpr int XL = XST / 1024 / 4;      // X load instructions per wave and stage
+  constexpr int AL = NB;                  // A load instructions per wave and stage
+  constexpr int LPW = XL + AL;
+  static_assert((D - 2) * LPW <= 63 && D >= 2, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) int8_t smem[D * STAGE];
+
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row0 = xcd_slot(blockIdx.x, gridDim.x) * 128;
+  const int rows = m - row0 < 128 ? m - row0 : 128;
+  const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x + (int64_t)row0 * ldx, int(rows * ldx * ES));
+  const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(a, r * k * 2);
+  const int nkb = (k + 63) / 64;
+  auto xswz = [](int row) { return XCH == 8 ? (row >> 1) & 7 : row & 15; };
+  auto aswz = [](int row) { return (row >> 1) & 7; };
+  // Load instruction q of a stage (1 KB) is issued by wave q % 4.
+  auto issue = [&](int t) {
+    const int f0 = t * 64;
+    int8_t* st = smem + (t % D) * STAGE;
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      const int q = wave + 4 * i;
+      const int row = q * (64 / XCH) + lane / XCH;
+      const int ch = (lane % XCH) ^ xswz(row);
+      const int f = f0 + ch * (16 / ES);
+      const unsigned off = f < k ? unsigned(row * ldx * ES + f * ES) : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void*)(st + q * 1024), 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < AL; ++i) {
+      const int q = wave + 4 * i;
+      const int row = q * 8 + lane / 8;
+      const int ch = (lane % 8) ^ aswz(row);
+      const int f = f0 + ch * 8;
+      const unsigned off = f < k ? unsigned(row * k * 2 + f * 2) : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void*)(st + XST + q * 1024), 16, off, 0,
+                                               0, 0);
+    }
+  };
+  const int lr = lane & 31, h = lane >> 5;
+  const int xrow = wave * 32 + lr;
+  auto x_operand = [&](const int8_t* xs, int c) -> bf16x8 {
+    if constexpr (ES == 2) {
+      const int ch = (4 * h + c) ^ xswz(xrow);
+      return *reinterpret_cast<const bf16x8*>(xs + xrow * XROW + ch * 16);
+    } else {
+      const int c0 = (8 * h + 2 * c) ^ xswz(xrow), c1 = (8 * h + 2 * c + 1) ^ xswz(xrow);
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(xs + xrow * XROW + c0 * 16);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(xs + xrow * XROW + c1 * 16);
+      const bf16x2 p0 = __builtin_convertvector(f32x2{lo.x, lo.y}, bf16x2);
+      const bf16x2 p1 = __builtin_convertvector(f32x2{lo.z, lo.w}, bf16x2);
+      const bf16x2 p2 = __builtin_convertvector(f32x2{hi.x, hi.y}, bf16x2);
+      const bf16x2 p3 = __builtin_convertvector(f32x2{hi.z, hi.w}, bf16x2);
+      return bf16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+    }
+  };
+  auto a_operand = [&](const int8_t* as, int b, int c) -> bf16x8 {
+    const int row = b * 32 + lr;
+    const int ch = (4 * h + c) ^ aswz(row);
+    return *reinterpret_cast<const bf16x8*>(as + row * 128 + ch * 16);
+  };
+
+  f32x16 acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = f32x16{};
+#pragma unroll
+  for (int t = 0; t < D - 1; ++t) issue(t);
+  for (int t = 0; t < nkb; ++t) {
+    // This wave's loads of stage t have landed once only those of the D - 2
+    // later stages may be in flight; after the barrier everybody's have, and
+    // everybody has finished with stage t - 1, whose slot is refilled.
+    waitvm<(D - 2) * LPW>();
+    barrier();
+    issue(t + D - 1);  // past the last block: out of range, reads zeros
+    const int8_t* st = smem + (t % D) * STAGE;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bf16x8 xo = x_operand(st, c);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xo, a_operand(st + XST, b, c), acc[b],
+                                                         0, 0, 0);
+    }
+  }
+  waitvm<0>();
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int orow = row0 + wave * 32 + 8 * (i / 4) + 4 * h + (i & 3);
+      const int ocol = b * 32 + lr;
+      if (orow < m && ocol < r) u[(int64_t)orow * ldu + ocol] = bf16_bits(scale * acc[b][i]);
+    }
+}
+
 // Y[128 x 128 tile] += U B^T.  Each wave owns 64 x 64 (2 x 2 blocks of
 // 32 x 32); the rank r is the contraction length (steps of 16).  The tile's
 // Y values are read, updated and written back (float32).
@@ -291,9 +408,33 @@ __global__ __launch_bounds__(256) void lora_up_add_kernel(const uint16_t* __rest
       }
 }
 
+template <typename InT, int NB>
+hipError_t launch_down_rows(const void* x, int64_t ldx, int m, int k, const uint16_t* a, int r,
+                            float scale, uint16_t* u, int64_t ldu, hipStream_t stream) {
+  // As many stages of (X 128 rows + A 32 NB rows) x 64 features as fit in
+  // 160 KB, at most 4.
+  constexpr int STAGE = 128 * 64 * int(sizeof(InT)) + 32 * NB * 128;
+  constexpr int D = (160 * 1024 / STAGE) < 4 ? (160 * 1024 / STAGE) : 4;
+  const int blocks = (m + 127) / 128;
+  hipLaunchKernelGGL((lora_down_rows_kernel<InT, NB, D>), dim3(blocks), dim3(256), 0, stream,
+                     static_cast<const InT*>(x), ldx, m, k, a, r, scale, u, ldu);
+  return hipGetLastError();
+}
+
 template <typename InT>
 hipError_t launch_down(const void* x, int64_t ldx, int m, int k, const uint16_t* a, int r,
                        float scale, uint16_t* u, int64_t ldu, hipStream_t stream) {
+  // Long X (a 128-row block for every CU): one workgroup per 128 rows and
+  // all of U's columns.  Otherwise 32 x 32 blocks of U, K split over waves.
+  if ((m + 127) / 128 >= device_cu_count()) {
+    switch ((r + 31) / 32) {
+      case 1: return launch_down_rows<InT, 1>(x, ldx, m, k, a, r, scale, u, ldu, stream);
+      case 2: return launch_down_rows<InT, 2>(x, ldx, m, k, a, r, scale, u, ldu, stream);
+      case 3: return launch_down_rows<InT, 3>(x, ldx, m, k, a, r, scale, u, ldu, stream);
+      case 4: return launch_down_rows<InT, 4>(x, ldx, m, k, a, r, scale, u, ldu, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   const int ncb = (r + 31) / 32;
   const int64_t blocks = int64_t((m + 31) / 32) * ncb;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
@@ -302,6 +443,7 @@ hipError_t launch_down(const void* x, int64_t ldx, int m, int k, const uint16_t*
                      static_cast<const InT*>(x), ldx, m, k, a, r, scale, u, ldu, ncb);
   return hipGetLastError();
 }
+static_assert(kLoraMaxRank == 128, "launch_down covers 1 to 4 column blocks");
 
 }  // namespace
 

@@ -192,7 +192,7 @@ convrot_status convrot_linear_grouped(const convrot_packed* x, const convrot_wei
 /*
  * convrot_lora_down: U = bf16(scale * X A^T).
  *   x : device [m, k] of x_dtype (CONVROT_F32 or CONVROT_BF16), row stride
- *       k <= ldx <= 2^22; float32 X is rounded to bfloat16 (nearest even) first
+ *       k <= ldx <= 2^21; float32 X is rounded to bfloat16 (nearest even) first
  *   a : device bfloat16 [rank, k], row stride k
  *   u : device bfloat16 [m, ldu] (output; columns rank .. ldu-1 untouched, so
  *       several adapters' U can share one buffer)

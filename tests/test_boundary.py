@@ -217,7 +217,7 @@ def test_lora_down_validation():
     assert _down(k=0) == cr.ERR_SHAPE
     assert _down(m=-1) == cr.ERR_SHAPE
     assert _down(ldx=512) == cr.ERR_SHAPE           # ldx < k
-    assert _down(ldx=(1 << 22) + 8) == cr.ERR_SHAPE
+    assert _down(ldx=(1 << 21) + 8) == cr.ERR_SHAPE
     assert _down(ldu=16) == cr.ERR_SHAPE            # ldu < rank
     assert _down(ldu=(1 << 20) + 8) == cr.ERR_SHAPE
     assert _down(dt=2) == cr.ERR_DTYPE

@@ -559,14 +559,16 @@ def test_linear_from_checkpoint(tmp_path):
 # ---------------------------------------------------------------------------
 # Low-rank adapter correction (bf16 operands, float32 accumulation)
 # ---------------------------------------------------------------------------
-# U = bf16(scale X A^T) on both sides, but the device rounds a float32 sum and
-# the oracle a float64 one, so an element of U may sit one bf16 unit apart
-# where the sum lies next to a rounding boundary.  Bounds:
-#   U: |dU| <= 2^-8 |U_or| + eps_U, eps_U = 2^-24 k |scale| sum|x||a| (float32
-#      accumulation), on at most 1% of elements;
-#   Y: |dY| <= (2^-8 |U_or| + eps_U) |B|^T + 2^-22 (|Y0| + |U||B|^T)
-#      (plus the convrot linear's own bound for a fused output), and the
-#      correction's aggregate L1 error <= 1e-3 of its L1 norm.
+# U = bf16(scale X A^T) on both sides, but the device rounds a float32 sum S32
+# and the oracle the exact sum S, so an element of U may sit one bf16 unit
+# apart where the sums straddle a rounding boundary.  With |S32 - S| <= eps_U
+# = 2^-24 k |scale| sum|x||a| (float32 accumulation) and half a bf16 unit
+# <= 2^-8 |v| (8 significant bits):
+#   U: |dU| <= 1/2 ulp(S32) + eps_U + 1/2 ulp(S) <= (2^-7 + 2^-14) |U_or|
+#      + 1.01 eps_U, on at most 1% of elements;
+#   Y: |dY| <= dU_bound |B|^T + 2^-22 (|Y0| + |U||B|^T) (plus the convrot
+#      linear's own bound for a fused output), and the correction's aggregate
+#      L1 error <= 1e-3 of its L1 norm.
 LORA_U_MISMATCH_FRAC = 1e-2
 
 
@@ -579,6 +581,10 @@ def _lora_case(m, k, n, rank, x_dtype, seed):
     return inp["x"], x64, ad
 
 
+def _u_bound(u_or, eps_u):
+    return (2.0**-7 + 2.0**-14) * np.abs(u_or) + 1.01 * eps_u
+
+
 def _lora_bounds(x64, ad):
     """(U_or, eps_U, per-element bound on the correction, correction)."""
     a64, b64, scale = ad["a64"], ad["b64"], ad["scale"]
@@ -586,13 +592,16 @@ def _lora_bounds(x64, ad):
     eps_u = 2.0**-24 * x64.shape[1] * abs(scale) * (np.abs(x64) @ np.abs(a64).T)
     corr = orc.lora_up(u_or, b64)
     mag = np.abs(u_or) @ np.abs(b64).T
-    bound = (2.0**-8 * np.abs(u_or) + eps_u) @ np.abs(b64).T + 2.0**-22 * mag
+    bound = _u_bound(u_or, eps_u) @ np.abs(b64).T + 2.0**-22 * mag
     return u_or, eps_u, bound, corr
 
 
 def _check_u(u_dev, u_or, eps_u, what):
     du = np.abs(u_dev.astype(np.float64) - u_or)
-    assert np.all(du <= 2.0**-8 * np.abs(u_or) + eps_u), f"{what}: U outside one bf16 unit"
+    bound = _u_bound(u_or, eps_u)
+    bad = du > bound
+    assert not bad.any(), (f"{what}: {np.count_nonzero(bad)} of {du.size} U elements outside one "
+                           f"bf16 unit, worst |dU|/bound {np.max(du / np.maximum(bound, 1e-300)):.3g}")
     frac = np.count_nonzero(du) / max(1, du.size)
     assert frac <= LORA_U_MISMATCH_FRAC, f"{what}: {frac:.3%} of U differs"
 
@@ -612,6 +621,8 @@ def _check_lora(u_dev, y_dev, x64, ad, what):
     (16, 1024, 512, 16, "f32"), (37, 1024, 700, 32, "bf16"), (300, 2048, 400, 48, "bf16"),
     (257, 3072, 3072, 64, "f32"), (1000, 3072, 1100, 128, "bf16"), (64, 16, 129, 96, "bf16"),
     (1, 4096, 33, 80, "f32"),
+    # long X: one workgroup per 128 rows (ragged M and K tails)
+    (32760, 1040, 64, 64, "bf16"), (32900, 256, 50, 128, "f32"), (32769, 48, 40, 16, "bf16"),
 ])
 def test_lora_parity(m, k, n, rank, dt):
     x, x64, ad = _lora_case(m, k, n, rank, dt, seed=m + rank)
