@@ -712,6 +712,47 @@ def test_linear_lora_fused_gelu_and_short_k():
     _fused_case(600, (2000,), (32,), gelu=True)
 
 
+@pytest.mark.parametrize("name", ["qkv_4096x3072x9216", "video_32760x5120x13824"])
+def test_linear_lora_full_size_sampled(name):
+    """Rank-64 adapters on every linear of a full-size workload, in the launch
+    the benchmark times (one U buffer shared by the adapters), checked on
+    sampled rows against the oracle's linear plus correction."""
+    w = wl.WORKLOADS[name]
+    inp = wl.generate(w)
+    g, rank = 256, 64
+    rows = _sample_rows(w.m, w.seed + 1, n=24)
+    _say(f"fused lora full {name}")
+    x = dev(inp["x"])
+    p = cr.pack_activations(x, g)
+    ws = [_prep(wt, b, g) for wt, b in zip(inp["weights"], inp["biases"])]
+    ads = [wl.lora_adapter(w.k, wt.shape[0], rank, m=0, seed=w.seed + 50 + i)
+           for i, wt in enumerate(inp["weights"])]
+    ucat = torch.empty((w.m, rank * len(ads)), dtype=torch.bfloat16, device="cuda")
+    adapters = []
+    for i, ad in enumerate(ads):
+        u = cr.lora_down(x, dev(ad["a"]), ad["scale"], out=ucat[:, i * rank:(i + 1) * rank])
+        adapters.append((u, dev(ad["b"])))
+    ys = cr.linear_lora(p, ws, adapters)
+    idx = torch.from_numpy(rows).cuda()
+    qx_or, sx_or = orc.pack_activations(inp["x64"][rows], g)
+    x_rows = inp["x64"][rows]
+    for i, (y, wt, b, ad) in enumerate(zip(ys, inp["weights"], inp["biases"], ads)):
+        yr = host(y[idx])
+        qw_or, sw_or = orc.quantize_weights(wt, g)
+        base = orc.linear(qx_or, sx_or, qw_or, sw_or, b)
+        _, _, lb, corr = _lora_bounds(x_rows, ad)
+        y_or = base + corr
+        bound = Y_ELEM * sx_or.astype(np.float64)[:, None] * sw_or.astype(np.float64)[None, :] \
+            * w.k * 127 + lb + 2.0**-22 * np.abs(y_or)
+        err = np.abs(yr.astype(np.float64) - y_or)
+        assert np.all(err <= bound), f"{name}[{i}]: bound exceeded by {np.max(err - bound):.3g}"
+        assert err.sum() / np.abs(y_or).sum() <= Y_MEAN_REL, f"{name}[{i}]"
+    u_rows = host(ucat[idx].float())
+    for i, ad in enumerate(ads):
+        u_or, eps_u, _, _ = _lora_bounds(x_rows, ad)
+        _check_u(u_rows[:, i * rank:(i + 1) * rank], u_or, eps_u, f"{name} U[{i}]")
+
+
 def test_linear_lora_rank_zero_matches_plain_linear():
     """With no adapter the fused path's values equal the plain linear's bit for bit
     (the same float32 expression A s_x s_w + b, evaluated at the tile end)."""
