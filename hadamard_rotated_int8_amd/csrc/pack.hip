@@ -463,7 +463,14 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const InT* __restrict__ 
 // natural layout by a byte transpose through the same LDS buffer and leave
 // as 16-byte stores.  A row's maximum satisfies |x| <= max, so
 // |x / s| <= 127 (1 + 2^-23) and the code needs no clamp.
-constexpr int kTStride = 272;  // floats per 16-lane group: 256 + 16 (bank offset)
+// The 16 x 16 float transpose of a 16-lane group: lane li writes its 16
+// values as row li (four 16-byte writes) and reads column li back.  Rows are
+// kTRow = 20 floats apart, so the 16 row starts of a write fall on 16
+// distinct 4-bank groups (with 16-float rows four lanes shared one); the
+// column reads stay 16 consecutive floats.  Groups are kTStride floats apart
+// (a multiple of 64 banks plus 16, so the four groups' reads do not collide).
+constexpr int kTRow = 20;
+constexpr int kTStride = 16 * kTRow + 16;
 
 // WPR waves share one row (rows longer than one wave holds): wave w of a
 // workgroup takes part w % WPR of row slot w / WPR, the parts' maxima meet in
@@ -510,10 +517,10 @@ __global__ __launch_bounds__(256) void pack_rows_lds_kernel(const InT* __restric
       for (int a = 0; a < 4; ++a) h4_reg_pq(v[a], v[a + 4], v[a + 8], v[a + 12]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<f32x4*>(tw + li * 16 + 4 * i) =
+        *reinterpret_cast<f32x4*>(tw + li * kTRow + 4 * i) =
             f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) t[c][i] = tw[i * 16 + li];
+      for (int i = 0; i < 16; ++i) t[c][i] = tw[i * kTRow + li];
     }
     const int nrow = row + nr;
     if (nrow < m) {
