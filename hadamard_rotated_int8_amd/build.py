@@ -22,7 +22,7 @@ LIB_NAME = "libconvrot.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "pack.hip", "wprep.hip", "gemm.hip", "lora.hip"]
+SOURCES = ["api.cpp", "pack.hip", "wprep.hip", "gemm.hip", "gemm_small.hip", "lora.hip"]
 
 # Packed-FP32 instructions are kept out of generated code on purpose.
 COMMON_FLAGS = [

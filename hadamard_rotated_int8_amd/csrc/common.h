@@ -4,12 +4,58 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #define CR_DEVICE __device__ __forceinline__
 
 namespace convrot {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kNumXcd = 8;     // accelerator complex dies; workgroups are dealt to them round robin
+constexpr int kVmMax = 63;     // largest vmcnt a wait can name
+// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format).
+constexpr int kBufferWord3 = 0x00020000;
+constexpr unsigned kOutOfRange = 0x80000000u;  // an offset past every resource
+
+// A raw buffer resource over [base, base + bytes): loads at offsets past the
+// end return zero (the hardware range check).
+CR_DEVICE __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes,
+                                           kBufferWord3);
+}
+
+// Position of workgroup b in a grid of n: workgroups go to the XCDs round
+// robin (b % 8), and each XCD takes a contiguous run of positions, so
+// neighbouring positions share that XCD's L2.
+CR_DEVICE int xcd_slot(int b, int n) {
+  const int xcd = b % kNumXcd, idx = b / kNumXcd;
+  const int q = n / kNumXcd, rem = n % kNumXcd;
+  return (xcd < rem) ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
+}
+
+// s_waitcnt vmcnt(N), other counters unchanged.  gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14].
+template <int N>
+CR_DEVICE void waitvm() {
+  static_assert(N >= 0 && N <= kVmMax, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+CR_DEVICE void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// A bare s_barrier: the waits are issued explicitly (a __syncthreads fence
+// would also drain loads still in flight for later stages), and the memory
+// clobber keeps the compiler from moving LDS accesses across it.
+CR_DEVICE void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// f(integral_constant<int, I>) for every I of the sequence, in order.
+template <int... I, typename F>
+CR_DEVICE void for_each_index(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
 
 // DPP controls (GCN "data parallel primitives" operand modifiers).
 constexpr int kDppQuadSwap1 = 0xB1;    // quad_perm [1,0,3,2]: lane ^ 1
@@ -45,5 +91,27 @@ CR_DEVICE float div_by_recip(float x, float b, float r) {
 }
 
 CR_DEVICE int clamp127(int q) { return max(-127, min(127, q)); }
+
+// erf(x) by Abramowitz & Stegun, Handbook of Mathematical Functions,
+// formula 7.1.26: for a >= 0, erf(a) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) e^{-a^2}
+// with t = 1 / (1 + p a), absolute error at most 1.5e-7; erf is odd.  About
+// a dozen VALU operations (hardware reciprocal and base-2 exponential)
+// instead of the device library's longer branch-and-select sequence, which
+// matters because the epilogue evaluates it for every output.
+CR_DEVICE float erf_as(float x) {
+  const float a = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, a, 1.0f));
+  float poly = __builtin_fmaf(t, 1.061405429f, -1.453152027f);
+  poly = __builtin_fmaf(t, poly, 1.421413741f);
+  poly = __builtin_fmaf(t, poly, -0.284496736f);
+  poly = __builtin_fmaf(t, poly, 0.254829592f);
+  poly *= t;
+  const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * a * a);  // e^{-a^2}
+  const float r = __builtin_fmaf(-poly, e, 1.0f);
+  return __builtin_copysignf(r, x);
+}
+
+// GELU, the erf form x * Phi(x) = x/2 (1 + erf(x / sqrt 2)).
+CR_DEVICE float gelu_erf(float y) { return 0.5f * y * (1.0f + erf_as(y * 0.70710678118654752f)); }
 
 }  // namespace convrot

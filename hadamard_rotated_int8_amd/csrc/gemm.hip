@@ -77,18 +77,12 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBM = 256;
 constexpr int kBN = 192;       // tile columns
 constexpr int kThreads = 256;  // 4 waves
-constexpr int kNumXcd = 8;
 constexpr int kGroupM = 4;
 constexpr int kMinSteps = 3;   // K steps per tile at least (see the header comment)
-constexpr int kVmMax = 63;     // largest vmcnt a wait can name
-// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format).
-constexpr int kBufferWord3 = 0x00020000;
-constexpr unsigned kOutOfRange = 0x80000000u;  // an offset past every resource
 
 // Output modes.  kModeF32 scales each value as it is stored; the tile-end
 // modes turn the whole tile into float32 values at its end (and add the
@@ -176,50 +170,6 @@ CR_DEVICE TileInfo tile_info(const GemmParams& p, int t) {
   return ti;
 }
 
-// Position of workgroup b inside a round of G tiles: each XCD (b % 8) gets a
-// contiguous run of tile indices.
-CR_DEVICE int round_slot(int b, int G) {
-  const int xcd = b % kNumXcd, idx = b / kNumXcd;
-  const int q = G / kNumXcd, r = G % kNumXcd;
-  return (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
-}
-
-// erf(x) by Abramowitz & Stegun, Handbook of Mathematical Functions,
-// formula 7.1.26: for a >= 0, erf(a) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) e^{-a^2}
-// with t = 1 / (1 + p a), absolute error at most 1.5e-7; erf is odd.  About
-// a dozen VALU operations (hardware reciprocal and base-2 exponential)
-// instead of the device library's longer branch-and-select sequence, which
-// matters because the epilogue evaluates it for every output.
-CR_DEVICE float erf_as(float x) {
-  const float a = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, a, 1.0f));
-  float poly = __builtin_fmaf(t, 1.061405429f, -1.453152027f);
-  poly = __builtin_fmaf(t, poly, 1.421413741f);
-  poly = __builtin_fmaf(t, poly, -0.284496736f);
-  poly = __builtin_fmaf(t, poly, 0.254829592f);
-  poly *= t;
-  const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * a * a);  // e^{-a^2}
-  const float r = __builtin_fmaf(-poly, e, 1.0f);
-  return __builtin_copysignf(r, x);
-}
-
-// GELU, the erf form x * Phi(x) = x/2 (1 + erf(x / sqrt 2)).
-CR_DEVICE float gelu_erf(float y) { return 0.5f * y * (1.0f + erf_as(y * 0.70710678118654752f)); }
-
-CR_DEVICE void barrier() {
-  // A bare s_barrier: the waits are issued explicitly, and the memory clobber
-  // keeps the compiler from moving LDS accesses across it.
-  asm volatile("s_barrier" ::: "memory");
-}
-
-// s_waitcnt vmcnt(N), other counters unchanged.  gfx9 encoding:
-// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14].
-template <int N>
-CR_DEVICE void waitvm_c() {
-  static_assert(N >= 0 && N <= kVmMax, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-CR_DEVICE void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Slot (MFMA index in [lo, n_slots)) of the i-th of n loads spread evenly
 // over a sub-step; -1 for no load at that slot.
@@ -227,17 +177,6 @@ constexpr int spread_piece(int idx, int lo, int n_slots, int n) {
   for (int i = 0; i < n; ++i)
     if (idx == lo + ((2 * i + 1) * (n_slots - lo)) / (2 * n)) return i;
   return -1;
-}
-
-// f(integral_constant<int, I>) for every I of the sequence, in order.
-template <int... I, typename F>
-CR_DEVICE void for_each_index(std::integer_sequence<int, I...>, F&& f) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-
-CR_DEVICE __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes,
-                                           kBufferWord3);
 }
 
 template <int BN, int MODE>
@@ -259,7 +198,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
   // whole kernel.
   int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = gridDim.x;
-  const int slot = round_slot(blockIdx.x, G);
+  const int slot = xcd_slot(blockIdx.x, G);
   const int ntiles = (p.total_tiles - slot + G - 1) / G;  // >= 1: grid <= tiles
   const int nk = p.nk;                                    // >= kMinSteps
   int M = p.M, K = p.K;
@@ -493,7 +432,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
     for (int i = 0; i < C::WPW; ++i) piece_w(i);
     end_w();
   }
-  waitvm_c<0>();
+  waitvm<0>();
   wait_lgkm0();
   barrier();
 #pragma unroll
@@ -624,7 +563,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
     }
     // Q_x of step g+1 and (issued a step earlier) Q_w of step g+1 have
     // landed once only this step's stores and Q_w loads may be in flight.
-    waitvm_c<C::WPW + NST>();
+    waitvm<C::WPW + NST>();
     wait_lgkm0();
     barrier();  // the next stages are readable by all, this step's are free
     begin_x();
@@ -827,7 +766,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
       store_group(Q, read_group_sx(Q));
     });
   }
-  waitvm_c<0>();  // no load into LDS may still be in flight at exit
+  waitvm<0>();  // no load into LDS may still be in flight at exit
 }
 
 template <int BN, int MODE>
@@ -868,6 +807,8 @@ int device_cu_count() {
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
+  int slices = 0;
+  if (gemm_split_wanted(a, device_cu_count(), &slices)) return launch_gemm_split(a, slices, stream);
   GemmParams p{};
   p.qx = a.qx;
   p.sx = a.sx;

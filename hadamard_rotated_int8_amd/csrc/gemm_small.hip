@@ -1,0 +1,249 @@
+// INT8 GEMM for outputs with few tiles (short M): split K.
+//
+// The same computation as gemm.hip, from the stable-diffusion.cpp page
+// "INT8 Convrot Safetensors", section "Runtime activation quantization":
+//   A[r, o] = sum_i Q_x[r, i] Q_w[o, i]   (int32),  Y = A s_x[r] s_w[o] + b[o].
+// The persistent kernel's 256 x 192 tiles leave most of the 256 CUs idle
+// when M is a few hundred rows (a 256 x 4096 x 4096 linear has 22 tiles).
+// Here the output is cut into 64 x 128 tiles and K into equal slices, so
+// that there are about two work items per CU:
+//   1. zero_kernel clears Y (viewed as int32);
+//   2. gemm_split_kernel computes one tile over one K slice and adds its
+//      int32 partial sums into Y with atomic adds.  Integer addition is exact
+//      and associative, so the result does not depend on the order in which
+//      the slices arrive;
+//   3. scale_kernel turns each int32 A into A s_x s_w + b in place (the same
+//      float32 expression as the persistent kernel's epilogue), then GELU
+//      when asked.  With int32 output the last step is skipped.
+// Operands are staged through LDS by direct-to-LDS loads of whole 128-byte
+// lines, swizzled like the persistent kernel's stages (chunk c of row r at
+// slot c ^ (r & 7) ^ ((r >> 3) & 1)), in a ring of 3 stages with one barrier
+// per 128-byte K step.  Rows past M or n and bytes past K read as zero.
+#include "common.h"
+#include "kernels.h"
+
+namespace convrot {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int kSM = 64;                 // tile rows (Q_x)
+constexpr int kSN = 128;                // tile columns (Q_w rows)
+constexpr int kSK = 128;                // K bytes per step
+constexpr int kSStages = 3;
+constexpr int kXBytes = kSM * kSK;      // 8 KB
+constexpr int kStage = kXBytes + kSN * kSK;  // + 16 KB
+constexpr int kPieces = kStage / 1024;  // 1 KB direct-to-LDS loads per stage
+constexpr int kLoadsPerWave = kPieces / 4;
+static_assert(kPieces % 4 == 0, "pieces split evenly over 4 waves");
+static_assert((kSStages - 2) * kLoadsPerWave <= kVmMax, "vmcnt range");
+
+struct SplitSeg {
+  const int8_t* qw;
+  int* acc;        // Y viewed as int32
+  int64_t ld;      // row stride of Y (elements)
+  int n;
+  int tiles_n;
+  int item0;       // first work item of this weight
+};
+
+struct SplitParams {
+  const int8_t* qx;
+  int M, K;
+  int steps;       // K steps per slice
+  int slices, tiles_m, nseg;
+  SplitSeg seg[kMaxGemmGroup];
+};
+
+CR_DEVICE int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// Work items are numbered weight, tile column, slice, tile row (fastest),
+// and dealt XCD by XCD, so the tile rows that read one slice of Q_w share
+// an L2.
+__global__ __launch_bounds__(256) void gemm_split_kernel(const SplitParams p) {
+  __shared__ __attribute__((aligned(1024))) int8_t smem[kSStages * kStage];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int item = xcd_slot(blockIdx.x, gridDim.x);
+  int s = 0;
+  for (int i = 1; i < p.nseg; ++i)
+    if (item >= p.seg[i].item0) s = i;
+  const SplitSeg& sg = p.seg[s];
+  const int local = item - sg.item0;
+  const int tm = local % p.tiles_m;
+  const int rest = local / p.tiles_m;
+  const int slice = rest % p.slices;
+  const int tn = rest / p.slices;
+  const int m0 = tm * kSM, n0 = tn * kSN;
+  const int K = p.K;
+  const int rows = p.M - m0 < kSM ? p.M - m0 : kSM;
+  const int cols = sg.n - n0 < kSN ? sg.n - n0 : kSN;
+  const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(p.qx + (int64_t)m0 * K, rows * K);
+  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(sg.qw + (int64_t)n0 * K, cols * K);
+  const int kb0 = slice * p.steps * kSK;  // first K byte of the slice
+
+  // Piece q (1 KB: rows 8q .. 8q+7 of the stage; Q_x pieces first) is loaded
+  // by wave q % 4.  Lane j fills slot j % 8 of row j / 8 with global chunk
+  // (j % 8) ^ swz(row).  Steps past the slice read the next slice's bytes
+  // into stages that are never consumed; bytes past K read as zero.
+  auto issue = [&](int t) {
+    int8_t* st = smem + (t % kSStages) * kStage;
+    const int kk = kb0 + t * kSK;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+      const int q = wave + 4 * i;
+      const bool is_x = q < kXBytes / 1024;
+      const int row = (is_x ? q : q - kXBytes / 1024) * 8 + lane / 8;
+      const int chunk = (lane & 7) ^ swz(row);
+      const int kc = kk + chunk * 16;
+      const unsigned off = kc < K ? unsigned(row * K + kc) : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_x ? xr : wr, (lds_void*)(st + q * 1024), 16, off,
+                                               0, 0, 0);
+    }
+  };
+
+  // Wave (wm, wn) = (wave / 2, wave % 2) owns rows 32 wm .. +31 and columns
+  // 64 wn .. +63 of the tile: two 32 x 32 accumulator blocks.  Lane l reads
+  // row l % 32 of a block, 16-byte chunk 2 kk + l / 32 of the step's K
+  // slice kk.
+  const int wm = wave >> 1, wn = wave & 1;
+  const int fr = lane & 31, fh = lane >> 5;
+  v16i acc[2] = {v16i{}, v16i{}};
+#pragma unroll
+  for (int t = 0; t < kSStages - 1; ++t) issue(t);
+  for (int t = 0; t < p.steps; ++t) {
+    // This wave's pieces of stage t have landed once only those of the
+    // stages after it may be in flight; after the barrier everybody's have,
+    // and stage t - 1 is free for the refill.
+    waitvm<(kSStages - 2) * kLoadsPerWave>();
+    barrier();
+    issue(t + kSStages - 1);
+    const int8_t* st = smem + (t % kSStages) * kStage;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int xrow = wm * 32 + fr;
+      const v4i xf = *reinterpret_cast<const v4i*>(st + xrow * kSK + (((2 * kk + fh) ^ swz(xrow)) << 4));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int wrow = wn * 64 + j * 32 + fr;
+        const v4i wf = *reinterpret_cast<const v4i*>(st + kXBytes + wrow * kSK +
+                                                     (((2 * kk + fh) ^ swz(wrow)) << 4));
+        acc[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf, wf, acc[j], 0, 0, 0);
+      }
+    }
+  }
+  waitvm<0>();  // no load into LDS may still be in flight at exit
+  // Accumulator register i of lane l: row 8 (i / 4) + 4 (l / 32) + i % 4,
+  // column l % 32 of the block.
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = n0 + wn * 64 + j * 32 + fr;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = m0 + wm * 32 + 8 * (i / 4) + 4 * fh + (i & 3);
+      if (row < p.M && col < sg.n) atomicAdd(sg.acc + (int64_t)row * sg.ld + col, acc[j][i]);
+    }
+  }
+}
+
+// Y[r, c] = 0 for r < m, c < n (row stride ld), grid-stride over rows.
+__global__ __launch_bounds__(256) void zero_kernel(int* __restrict__ y, int64_t ld, int m, int n) {
+  for (int r = blockIdx.y; r < m; r += gridDim.y)
+    for (int c = blockIdx.x * 256 + threadIdx.x; c < n; c += gridDim.x * 256)
+      y[(int64_t)r * ld + c] = 0;
+}
+
+// Y[r, c] = act(float(A[r, c]) s_x[r] s_w[c] + b[c]) in place.
+template <bool GELU>
+__global__ __launch_bounds__(256) void scale_kernel(float* __restrict__ y, int64_t ld, int m, int n,
+                                                    const float* __restrict__ sx,
+                                                    const float* __restrict__ sw,
+                                                    const float* __restrict__ bias) {
+  for (int r = blockIdx.y; r < m; r += gridDim.y) {
+    const float s = sx[r];
+    for (int c = blockIdx.x * 256 + threadIdx.x; c < n; c += gridDim.x * 256) {
+      float* yp = y + (int64_t)r * ld + c;
+      const int a = __float_as_int(*yp);
+      float v = __builtin_fmaf((float)a * s, sw[c], bias ? bias[c] : 0.f);
+      if (GELU) v = gelu_erf(v);
+      *yp = v;
+    }
+  }
+}
+
+dim3 elementwise_grid(int64_t m, int64_t n) {
+  const int64_t gx = (n + 255) / 256 < 16 ? (n + 255) / 256 : 16;
+  const int64_t gy = m < 4096 ? m : 4096;
+  return dim3(unsigned(gx), unsigned(gy));
+}
+
+}  // namespace
+
+// Pick the path from two estimates fitted to MI355X measurements of both
+// kernels at short M (16 .. 768 rows, K 1024 .. 12288, N 512 .. 13824): the
+// persistent kernel takes about 3 us + 1.2 us per 128-byte K step for each
+// round of 256 x 192 tiles over the CUs; the split path about 8 us plus its
+// operand intake (every 64 x 128 tile reads 24 KB per K step) at 6.5 TB/s,
+// the rate the CUs' direct-to-LDS loads sustain here.  The split path is
+// taken when it is estimated 15 % faster, only while the persistent kernel
+// has fewer tiles than CUs.
+bool gemm_split_wanted(const GemmArgs& a, int cus, int* slices) {
+  if (a.lora) return false;
+  const int64_t steps = (a.k + kSK - 1) / kSK;
+  int64_t big = 0, small = 0;
+  for (int i = 0; i < a.count; ++i) {
+    big += ((a.m + 255) / 256) * ((a.w[i].n + 191) / 192);
+    small += ((a.m + kSM - 1) / kSM) * ((a.w[i].n + kSN - 1) / kSN);
+  }
+  if (big >= cus || steps < 2) return false;
+  const double main_us = 3.0 + 1.2 * double(steps);
+  const double split_us = 8.0 + double(small) * double(steps) * kStage / 6.5e6;
+  if (!(split_us < 0.85 * main_us)) return false;
+  // About two work items per CU, each slice at least 2 K steps.
+  int64_t s = (2 * cus + small - 1) / small;
+  if (s > steps / 2) s = steps / 2;
+  if (s < 1) s = 1;
+  *slices = int(s);
+  return true;
+}
+
+hipError_t launch_gemm_split(const GemmArgs& a, int slices, hipStream_t stream) {
+  SplitParams p{};
+  p.qx = a.qx;
+  p.M = int(a.m);
+  p.K = int(a.k);
+  const int steps = int((a.k + kSK - 1) / kSK);
+  p.steps = (steps + slices - 1) / slices;
+  p.slices = (steps + p.steps - 1) / p.steps;
+  p.tiles_m = int((a.m + kSM - 1) / kSM);
+  p.nseg = a.count;
+  int items = 0;
+  for (int i = 0; i < a.count; ++i) {
+    SplitSeg& sg = p.seg[i];
+    sg.qw = a.w[i].qw;
+    sg.acc = static_cast<int*>(a.w[i].y);
+    sg.ld = a.w[i].ldy;
+    sg.n = int(a.w[i].n);
+    sg.tiles_n = (sg.n + kSN - 1) / kSN;
+    sg.item0 = items;
+    items += sg.tiles_n * p.slices * p.tiles_m;
+    hipLaunchKernelGGL(zero_kernel, elementwise_grid(a.m, a.w[i].n), dim3(256), 0, stream, sg.acc,
+                       sg.ld, p.M, sg.n);
+  }
+  hipLaunchKernelGGL(gemm_split_kernel, dim3(unsigned(items)), dim3(256), 0, stream, p);
+  if (!a.raw_i32) {
+    for (int i = 0; i < a.count; ++i) {
+      float* y = static_cast<float*>(a.w[i].y);
+      const dim3 grid = elementwise_grid(a.m, a.w[i].n);
+      if (a.gelu)
+        hipLaunchKernelGGL(scale_kernel<true>, grid, dim3(256), 0, stream, y, a.w[i].ldy, p.M,
+                           int(a.w[i].n), a.sx, a.w[i].sw, a.w[i].bias);
+      else
+        hipLaunchKernelGGL(scale_kernel<false>, grid, dim3(256), 0, stream, y, a.w[i].ldy, p.M,
+                           int(a.w[i].n), a.sx, a.w[i].sw, a.w[i].bias);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace convrot

@@ -12,8 +12,6 @@
 // (v_mfma_f32_32x32x16_bf16, float32 accumulation).  Operands go straight
 // from global memory into the MFMA register layout; no LDS staging.  The
 // down projection streams X once from HBM (A is small and stays in L2).
-#include <utility>
-
 #include "common.h"
 #include "kernels.h"
 
@@ -28,15 +26,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format).
-constexpr int kBufferWord3 = 0x00020000;
-constexpr unsigned kOutOfRange = 0x80000000u;  // an offset past every resource
-
-CR_DEVICE __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes,
-                                           kBufferWord3);
-}
-
 // float32 -> bfloat16 bits, round to nearest even (v_cvt_pk_bf16_f32).
 CR_DEVICE unsigned short bf16_bits(float f) {
   const bf16x2 r = __builtin_convertvector(f32x2{f, 0.f}, bf16x2);
@@ -50,36 +39,6 @@ CR_DEVICE bf16x8 as_bf16x8(u16x8 v) { return __builtin_bit_cast(bf16x8, v); }
 CR_DEVICE u16x8 load8(const uint16_t* __restrict__ p, bool ok) {
   if (!ok) return u16x8{};
   return __builtin_bit_cast(u16x8, *reinterpret_cast<const u32x4*>(p));
-}
-
-// Position of workgroup b in a grid of n: workgroups go to the 8 XCDs round
-// robin, and each XCD takes a contiguous run of positions.
-CR_DEVICE int xcd_slot(int b, int n) {
-  const int xcd = b % 8, idx = b / 8;
-  const int q = n / 8, rem = n % 8;
-  return (xcd < rem) ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// s_waitcnt vmcnt(N), other counters unchanged (gfx9 encoding:
-// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
-template <int N>
-CR_DEVICE void waitvm() {
-  static_assert(N >= 0 && N <= 63, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-CR_DEVICE void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-// A bare s_barrier (the waits are explicit; a __syncthreads fence would also
-// drain the loads still in flight for later stages).  The memory clobber
-// keeps LDS accesses on their side of it.
-CR_DEVICE void barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-// f(integral_constant<int, I>) for every I of the sequence, in order.
-template <int... I, typename F>
-CR_DEVICE void for_each_index(std::integer_sequence<int, I...>, F&& f) {
-  (f(std::integral_constant<int, I>{}), ...);
 }
 
 // U[32 x 32 block] = bf16(scale * X A^T).  The workgroup's 4 waves share the

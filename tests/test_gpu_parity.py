@@ -295,6 +295,21 @@ def test_gemm_raw_int32_many_tiles_per_workgroup(m, k, n):
     assert np.array_equal(a.astype(np.int64), orc.int_gemm(qx, qw))
 
 
+@pytest.mark.parametrize("m,k,n", [(64, 12288, 256), (1, 3072, 5000), (96, 130064, 40)])
+def test_gemm_raw_int32_split_k(m, k, n):
+    """Short outputs take the split-K path (64 x 128 tiles, K cut into slices
+    whose int32 partial sums meet in Y by atomic adds): many slices, a single
+    row, and K near its limit with a ragged last slice."""
+    rng = np.random.default_rng(m + n)
+    qx = rng.integers(-127, 128, size=(m, k)).astype(np.int8)
+    qw = rng.integers(-127, 128, size=(n, k)).astype(np.int8)
+    _say(f"gemm split-K m={m} k={k} n={n}")
+    a = _raw_gemm(qx, qw)
+    assert np.array_equal(a.astype(np.int64), orc.int_gemm(qx, qw))
+    b = _raw_gemm(qx, qw)  # the atomic sums are exact, hence repeatable
+    assert np.array_equal(a, b)
+
+
 def test_gemm_raw_int32_extremes_at_max_k():
     k = cr.MAX_K
     qx = np.full((2, k), 127, dtype=np.int8)
