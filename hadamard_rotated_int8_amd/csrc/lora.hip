@@ -9,9 +9,11 @@
 //   Y[m, n] += U B^T           (lora_up_add_kernel, on the convrot output Y;
 //                               the GEMM can also add it in its epilogue)
 // Both are small dense contractions on the bf16 matrix cores
-// (v_mfma_f32_32x32x16_bf16, float32 accumulation).  Operands go straight
-// from global memory into the MFMA register layout; no LDS staging.  The
-// down projection streams X once from HBM (A is small and stays in L2).
+// (v_mfma_f32_32x32x16_bf16, float32 accumulation).  The down projection
+// streams X from HBM through LDS stages filled by direct-to-LDS loads (A is
+// small and stays in L2): 32 x 32 blocks of U with K split over the waves
+// for short X, 128-row blocks for long X.  The up-add pass takes U and B
+// (small, L2-resident) straight from global memory into the MFMA registers.
 #include "common.h"
 #include "kernels.h"
 
