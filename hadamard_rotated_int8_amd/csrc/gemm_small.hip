@@ -6,7 +6,7 @@
 // The persistent kernel's 256 x 192 tiles leave most of the 256 CUs idle
 // when M is a few hundred rows (a 256 x 4096 x 4096 linear has 22 tiles).
 // Here the output is cut into 64 x 128 tiles and K into equal slices, so
-// that there are about two work items per CU:
+// that there is about one work item per CU:
 //   1. zero_kernel clears Y (viewed as int32);
 //   2. gemm_split_kernel computes one tile over one K slice and adds its
 //      int32 partial sums into Y with atomic adds.  Integer addition is exact
@@ -17,8 +17,10 @@
 //      when asked.  With int32 output the last step is skipped.
 // Operands are staged through LDS by direct-to-LDS loads of whole 128-byte
 // lines, swizzled like the persistent kernel's stages (chunk c of row r at
-// slot c ^ (r & 7) ^ ((r >> 3) & 1)), in a ring of 3 stages with one barrier
-// per 128-byte K step.  Rows past M or n and bytes past K read as zero.
+// slot c ^ (r & 7) ^ ((r >> 3) & 1)), double-buffered (the next step's lines
+// load while this step's MFMAs run; a third stage measured no faster) with
+// one barrier per 128-byte K step.  Rows past M or n and bytes past K read
+// as zero.
 #include "common.h"
 #include "kernels.h"
 
@@ -31,7 +33,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 constexpr int kSM = 64;                 // tile rows (Q_x)
 constexpr int kSN = 128;                // tile columns (Q_w rows)
 constexpr int kSK = 128;                // K bytes per step
-constexpr int kSStages = 3;
+constexpr int kSStages = 2;
 constexpr int kXBytes = kSM * kSK;      // 8 KB
 constexpr int kStage = kXBytes + kSN * kSK;  // + 16 KB
 constexpr int kPieces = kStage / 1024;  // 1 KB direct-to-LDS loads per stage
@@ -199,8 +201,9 @@ bool gemm_split_wanted(const GemmArgs& a, int cus, int* slices) {
   const double main_us = 3.0 + 1.2 * double(steps);
   const double split_us = 8.0 + double(small) * double(steps) * kStage / 6.5e6;
   if (!(split_us < 0.85 * main_us)) return false;
-  // About two work items per CU, each slice at least 2 K steps.
-  int64_t s = (2 * cus + small - 1) / small;
+  // About one work item per CU (measured 10-15 % faster than two: fewer
+  // atomic partial sums), each slice at least 2 K steps.
+  int64_t s = (cus + small - 1) / small;
   if (s > steps / 2) s = steps / 2;
   if (s < 1) s = 1;
   *slices = int(s);
