@@ -146,7 +146,8 @@ convrot_status convrot_pack_activations(const void* x, int32_t x_dtype, int64_t 
  * quantization]:
  *   A[r, o] = sum_i Q_x[r, i] Q_w[o, i]               (exact int32)
  *   Y[r, o] = A[r, o] * s_x[r] * s_w[o] + b[o]        (float32; then act)
- * y_dtype CONVROT_F32 writes Y (float32 [m, n], row stride ldy >= n);
+ * y_dtype CONVROT_F32 writes Y (float32 [m, n], row stride ldy >= n; Y must
+ * not overlap the inputs);
  * y_dtype CONVROT_I32 writes the raw int32 A (no scale, bias or act; act must
  * be CONVROT_ACT_NONE).  act CONVROT_ACT_GELU applies x*Phi(x) to Y.
  * The packed activation and the weights must have the same k and the same
@@ -163,7 +164,9 @@ convrot_status convrot_linear(const convrot_packed* x, const convrot_weights* w,
  * ([ICS, Runtime activation quantization]), e.g. the Q, K and V projections
  * of an attention block.  Weight i writes y[i] (row stride ldy[i] >= w[i].n);
  * semantics per weight are those of convrot_linear, with one y_dtype and one
- * act for all.  Weights with n == 0 are skipped.
+ * act for all.  Weights with n == 0 are skipped.  The outputs must not
+ * overlap one another or any input (short outputs are accumulated in place,
+ * as int32 partial sums, before they are scaled).
  *   w   : host array of `count` convrot_weights (device pointers inside)
  *   y   : host array of `count` device output pointers
  *   ldy : host array of `count` row strides
