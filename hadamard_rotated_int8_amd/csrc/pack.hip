@@ -33,6 +33,15 @@
 // absmax is a wave reduction.  No LDS and no barriers: a workgroup is just
 // four independent rows, and every row of the matrix can be in flight at
 // once, which is what an HBM-bound pass needs.
+//
+// G = 64 and 256 (pack_rows_lds_kernel, the common DiT case): the same
+// row-per-wave structure, but digits 2-3 reach registers by a 16 x 16
+// transpose through LDS inside each group of 16 lanes (rows padded against
+// bank conflicts), so every butterfly stage is a register stage; the codes
+// return by a byte transpose and leave as 16-byte stores; float32 rows are
+// loaded as whole 1 KB lines and handed to their lanes through LDS; rows
+// longer than 8192 features are split over 2 or 4 waves whose maxima meet
+// in LDS.
 #include <atomic>
 #include <type_traits>
 
