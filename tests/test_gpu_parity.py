@@ -420,6 +420,29 @@ def test_linear_grouped_raw_and_strided_outputs():
     assert torch.count_nonzero(big[:, 456:]) == 0
 
 
+def test_linear_grouped_float_outputs_in_one_buffer():
+    """Short outputs (split-K path): float32 outputs as column slices of one
+    wide buffer; the clearing, atomic sums and scaling stay inside each
+    output's columns."""
+    inp = wl.generate(wl.GSWEEP, m=200, n_limit=600)
+    g = 256
+    wt = inp["weights"][0]
+    parts = [(wt[:250], inp["biases"][0][:250]), (wt[250:450], None), (wt[450:600], inp["biases"][0][450:600])]
+    p = cr.pack_activations(dev(inp["x"]), g)
+    ws = [_prep(w_, b_, g) for w_, b_ in parts]
+    big = torch.full((200, 640), 5.0, dtype=torch.float32, device="cuda")
+    outs = [big[:, 0:250], big[:, 250:450], big[:, 452:602]]
+    _say("linear grouped float32, outputs in one buffer")
+    cr.linear_grouped(p, ws, outs=outs)
+    qx_or, sx_or = orc.pack_activations(inp["x64"], g)
+    bh = host(big)
+    for (w_, b_), o, sl in zip(parts, outs, (slice(0, 250), slice(250, 450), slice(452, 602))):
+        qw_or, sw_or = orc.quantize_weights(w_, g)
+        check_y(bh[:, sl], orc.linear(qx_or, sx_or, qw_or, sw_or, b_), sx_or, sw_or, 4096,
+                what=f"slice {sl.start}")
+    assert np.all(bh[:, 450:452] == 5.0) and np.all(bh[:, 602:] == 5.0), "columns between outputs written"
+
+
 def test_linear_without_bias_and_zero_weight_row():
     inp = wl.generate(wl.TINY)
     wt = inp["weights"][0].copy()
