@@ -15,12 +15,16 @@
 //   3. scale_kernel turns each int32 A into A s_x s_w + b in place (the same
 //      float32 expression as the persistent kernel's epilogue), then GELU
 //      when asked.  With int32 output the last step is skipped.
+// With a single slice (tiny outputs, where the extra launches dominate) the
+// kernel stores the finished values itself and steps 1 and 3 are skipped.
 // Operands are staged through LDS by direct-to-LDS loads of whole 128-byte
 // lines, swizzled like the persistent kernel's stages (chunk c of row r at
 // slot c ^ (r & 7) ^ ((r >> 3) & 1)), double-buffered (the next step's lines
 // load while this step's MFMAs run; a third stage measured no faster) with
 // one barrier per 128-byte K step.  Rows past M or n and bytes past K read
 // as zero.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -43,6 +47,8 @@ static_assert((kSStages - 2) * kLoadsPerWave <= kVmMax, "vmcnt range");
 
 struct SplitSeg {
   const int8_t* qw;
+  const float* sw;   // direct mode: column scales and bias (or null)
+  const float* bias;
   int* acc;        // Y viewed as int32
   int64_t ld;      // row stride of Y (elements)
   int n;
@@ -52,6 +58,7 @@ struct SplitSeg {
 
 struct SplitParams {
   const int8_t* qx;
+  const float* sx;   // direct mode: row scales
   int M, K;
   int steps;       // K steps per slice
   int slices, tiles_m, nseg;
@@ -63,6 +70,9 @@ CR_DEVICE int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 // Work items are numbered weight, tile column, slice, tile row (fastest),
 // and dealt XCD by XCD, so the tile rows that read one slice of Q_w share
 // an L2.
+// MODE 0: add int32 partial sums atomically; one slice only: 1 stores float32
+// A s_x s_w + b, 2 the same through GELU, 3 the int32 A.
+template <int MODE>
 __global__ __launch_bounds__(256) void gemm_split_kernel(const SplitParams p) {
   __shared__ __attribute__((aligned(1024))) int8_t smem[kSStages * kStage];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -143,7 +153,18 @@ __global__ __launch_bounds__(256) void gemm_split_kernel(const SplitParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int row = m0 + wm * 32 + 8 * (i / 4) + 4 * fh + (i & 3);
-      if (row < p.M && col < sg.n) atomicAdd(sg.acc + (int64_t)row * sg.ld + col, acc[j][i]);
+      if (row < p.M && col < sg.n) {
+        if constexpr (MODE == 0) {
+          atomicAdd(sg.acc + (int64_t)row * sg.ld + col, acc[j][i]);
+        } else if constexpr (MODE == 3) {
+          sg.acc[(int64_t)row * sg.ld + col] = acc[j][i];
+        } else {
+          float v = __builtin_fmaf((float)acc[j][i] * p.sx[row], sg.sw[col],
+                                   sg.bias ? sg.bias[col] : 0.f);
+          if constexpr (MODE == 2) v = gelu_erf(v);
+          reinterpret_cast<float*>(sg.acc)[(int64_t)row * sg.ld + col] = v;
+        }
+      }
     }
   }
 }
@@ -181,14 +202,16 @@ dim3 elementwise_grid(int64_t m, int64_t n) {
 
 }  // namespace
 
-// Pick the path from two estimates fitted to MI355X measurements of both
-// kernels at short M (16 .. 768 rows, K 1024 .. 12288, N 512 .. 13824): the
+// Pick the path from estimates fitted to MI355X measurements of the kernels
+// at short M (16 .. 768 rows, K 1024 .. 12288, N 512 .. 13824): the
 // persistent kernel takes about 3 us + 1.2 us per 128-byte K step for each
-// round of 256 x 192 tiles over the CUs; the split path about 8 us plus its
-// operand intake (every 64 x 128 tile reads 24 KB per K step) at 6.5 TB/s,
-// the rate the CUs' direct-to-LDS loads sustain here.  The split path is
-// taken when it is estimated 15 % faster, only while the persistent kernel
-// has fewer tiles than CUs.
+// round of 256 x 192 tiles over the CUs; the split path with atomic partial
+// sums about 8 us (three launches) plus its operand intake (every 64 x 128
+// tile reads 24 KB per K step) at 6.5 TB/s, the rate the CUs' direct-to-LDS
+// loads sustain here; one slice with direct stores about 3 us + 0.6 us per
+// K step and round of 64 x 128 tiles.  The cheaper split form is taken when
+// it is estimated 15 % faster than the persistent kernel, only while that
+// kernel has fewer tiles than CUs.
 bool gemm_split_wanted(const GemmArgs& a, int cus, int* slices) {
   if (a.lora) return false;
   const int64_t steps = (a.k + kSK - 1) / kSK;
@@ -199,13 +222,15 @@ bool gemm_split_wanted(const GemmArgs& a, int cus, int* slices) {
   }
   if (big >= cus || steps < 2) return false;
   const double main_us = 3.0 + 1.2 * double(steps);
-  const double split_us = 8.0 + double(small) * double(steps) * kStage / 6.5e6;
-  if (!(split_us < 0.85 * main_us)) return false;
+  const double atomic_us = 8.0 + double(small) * double(steps) * kStage / 6.5e6;
+  const double direct_us = 3.0 + 0.6 * double(steps) * double((small + cus - 1) / cus);
+  if (!(std::min(atomic_us, direct_us) < 0.85 * main_us)) return false;
   // About one work item per CU (measured 10-15 % faster than two: fewer
-  // atomic partial sums), each slice at least 2 K steps.
+  // atomic partial sums), each slice at least 2 K steps; one slice when
+  // direct stores are estimated cheaper.
   int64_t s = (cus + small - 1) / small;
   if (s > steps / 2) s = steps / 2;
-  if (s < 1) s = 1;
+  if (s < 1 || direct_us <= atomic_us) s = 1;
   *slices = int(s);
   return true;
 }
@@ -213,6 +238,7 @@ bool gemm_split_wanted(const GemmArgs& a, int cus, int* slices) {
 hipError_t launch_gemm_split(const GemmArgs& a, int slices, hipStream_t stream) {
   SplitParams p{};
   p.qx = a.qx;
+  p.sx = a.sx;
   p.M = int(a.m);
   p.K = int(a.k);
   const int steps = int((a.k + kSK - 1) / kSK);
@@ -220,29 +246,42 @@ hipError_t launch_gemm_split(const GemmArgs& a, int slices, hipStream_t stream) 
   p.slices = (steps + p.steps - 1) / p.steps;
   p.tiles_m = int((a.m + kSM - 1) / kSM);
   p.nseg = a.count;
+  // One slice: each tile's sums are final and are stored directly.
+  const bool direct = p.slices == 1;
   int items = 0;
   for (int i = 0; i < a.count; ++i) {
     SplitSeg& sg = p.seg[i];
     sg.qw = a.w[i].qw;
+    sg.sw = a.w[i].sw;
+    sg.bias = a.w[i].bias;
     sg.acc = static_cast<int*>(a.w[i].y);
     sg.ld = a.w[i].ldy;
     sg.n = int(a.w[i].n);
     sg.tiles_n = (sg.n + kSN - 1) / kSN;
     sg.item0 = items;
     items += sg.tiles_n * p.slices * p.tiles_m;
-    hipLaunchKernelGGL(zero_kernel, elementwise_grid(a.m, a.w[i].n), dim3(256), 0, stream, sg.acc,
-                       sg.ld, p.M, sg.n);
+    if (!direct)
+      hipLaunchKernelGGL(zero_kernel, elementwise_grid(a.m, a.w[i].n), dim3(256), 0, stream,
+                         sg.acc, sg.ld, p.M, sg.n);
   }
-  hipLaunchKernelGGL(gemm_split_kernel, dim3(unsigned(items)), dim3(256), 0, stream, p);
-  if (!a.raw_i32) {
+  const dim3 grid(static_cast<unsigned>(items));
+  if (!direct)
+    hipLaunchKernelGGL(gemm_split_kernel<0>, grid, dim3(256), 0, stream, p);
+  else if (a.raw_i32)
+    hipLaunchKernelGGL(gemm_split_kernel<3>, grid, dim3(256), 0, stream, p);
+  else if (a.gelu)
+    hipLaunchKernelGGL(gemm_split_kernel<2>, grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(gemm_split_kernel<1>, grid, dim3(256), 0, stream, p);
+  if (!direct && !a.raw_i32) {
     for (int i = 0; i < a.count; ++i) {
       float* y = static_cast<float*>(a.w[i].y);
-      const dim3 grid = elementwise_grid(a.m, a.w[i].n);
+      const dim3 eg = elementwise_grid(a.m, a.w[i].n);
       if (a.gelu)
-        hipLaunchKernelGGL(scale_kernel<true>, grid, dim3(256), 0, stream, y, a.w[i].ldy, p.M,
+        hipLaunchKernelGGL(scale_kernel<true>, eg, dim3(256), 0, stream, y, a.w[i].ldy, p.M,
                            int(a.w[i].n), a.sx, a.w[i].sw, a.w[i].bias);
       else
-        hipLaunchKernelGGL(scale_kernel<false>, grid, dim3(256), 0, stream, y, a.w[i].ldy, p.M,
+        hipLaunchKernelGGL(scale_kernel<false>, eg, dim3(256), 0, stream, y, a.w[i].ldy, p.M,
                            int(a.w[i].n), a.sx, a.w[i].sw, a.w[i].bias);
     }
   }

@@ -471,6 +471,25 @@ def test_linear_gelu_epilogue():
     check_y(y, y_or, sx_or, sw_or, 3072, gelu=True, what="gelu")
 
 
+@pytest.mark.parametrize("m,n", [(16, 512), (64, 1000)])
+def test_linear_gelu_short_output(m, n):
+    """GELU on short outputs (the split path's single-slice form, which
+    stores the finished values itself)."""
+    inp = wl.generate(wl.MLP, m=m, n_limit=n)
+    w = wl.Workload(name="short", m=m, k=1024, x_dtype="bf16", seed=9, linears=(),
+                    channel_lognormal=True)
+    xin = wl.generate(w)
+    wt = inp["weights"][0][:, :1024].copy()
+    b = inp["biases"][0]
+    p = cr.pack_activations(dev(xin["x"]), 256)
+    _say(f"linear gelu short m={m} n={n}")
+    y = host(cr.linear(p, _prep(wt, b, 256), gelu=True))
+    qx_or, sx_or = orc.pack_activations(xin["x64"], 256)
+    qw_or, sw_or = orc.quantize_weights(wt, 256)
+    y_or = orc.linear(qx_or, sx_or, qw_or, sw_or, b, act="gelu")
+    check_y(y, y_or, sx_or, sw_or, 1024, gelu=True, what=f"gelu short {m}x{n}")
+
+
 def test_mlp_pair():
     """DiT MLP: up (GELU fused) then down on the float32 GELU output."""
     w = wl.MLP
