@@ -38,7 +38,7 @@ ACT_GELU = 1
 MAX_K = 133136
 MAX_LOG4_GROUP = 7
 MAX_GROUPED = 8
-MAX_LORA_RANK = 128
+MAX_LORA_RANK = 256
 
 EXPORTED = (
     "convrot_quantize_weights",

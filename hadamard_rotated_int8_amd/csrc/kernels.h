@@ -55,7 +55,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 bool gemm_split_wanted(const GemmArgs& a, int cus, int* slices);
 hipError_t launch_gemm_split(const GemmArgs& a, int slices, hipStream_t stream);
 
-constexpr int kLoraMaxRank = 128;        // adapter ranks 16, 32, ..., 128
+constexpr int kLoraMaxRank = 256;        // adapter ranks 16, 32, ..., 256
 constexpr int64_t kLoraMaxLdu = 1 << 20;  // U row stride limit (32-bit buffer offsets)
 constexpr int64_t kLoraMaxLdx = 1 << 21;  // X row stride limit of the down projection (same)
 

@@ -385,9 +385,10 @@ hipError_t launch_down_rows(const void* x, int64_t ldx, int m, int k, const uint
 template <typename InT>
 hipError_t launch_down(const void* x, int64_t ldx, int m, int k, const uint16_t* a, int r,
                        float scale, uint16_t* u, int64_t ldu, hipStream_t stream) {
-  // Long X (a 128-row block for every CU): one workgroup per 128 rows and
-  // all of U's columns.  Otherwise 32 x 32 blocks of U, K split over waves.
-  if ((m + 127) / 128 >= device_cu_count()) {
+  // Long X (a 128-row block for every CU) and rank <= 128: one workgroup per
+  // 128 rows and all of U's columns.  Otherwise 32 x 32 blocks of U, K split
+  // over waves (any rank).
+  if ((m + 127) / 128 >= device_cu_count() && r <= 128) {
     switch ((r + 31) / 32) {
       case 1: return launch_down_rows<InT, 1>(x, ldx, m, k, a, r, scale, u, ldu, stream);
       case 2: return launch_down_rows<InT, 2>(x, ldx, m, k, a, r, scale, u, ldu, stream);
@@ -404,7 +405,7 @@ hipError_t launch_down(const void* x, int64_t ldx, int m, int k, const uint16_t*
                      static_cast<const InT*>(x), ldx, m, k, a, r, scale, u, ldu, ncb);
   return hipGetLastError();
 }
-static_assert(kLoraMaxRank == 128, "launch_down covers 1 to 4 column blocks");
+static_assert(kLoraMaxRank % 16 == 0, "ranks are multiples of 16");
 
 }  // namespace
 

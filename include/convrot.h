@@ -51,7 +51,7 @@ extern "C" {
 #define CONVROT_MAX_K 133136      /* largest k with k % 16 == 0 and k*127*127 < 2^31 */
 #define CONVROT_MAX_LOG4_GROUP 7  /* group sizes 1, 4, 16, ..., 16384 */
 #define CONVROT_MAX_GROUPED 8     /* weight matrices per convrot_linear_grouped call */
-#define CONVROT_MAX_LORA_RANK 128 /* adapter ranks 16, 32, ..., 128 */
+#define CONVROT_MAX_LORA_RANK 256 /* adapter ranks 16, 32, ..., 256 */
 
 typedef enum convrot_status {
   CONVROT_OK = 0,

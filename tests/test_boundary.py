@@ -214,7 +214,7 @@ def test_lora_rank_limits_match_header():
     assert int(re.search(r"#define CONVROT_MAX_LORA_RANK (\d+)", text).group(1)) == cr.MAX_LORA_RANK
 
 
-@pytest.mark.parametrize("r", [0, 8, 15, 24, 136, 144, -16])
+@pytest.mark.parametrize("r", [0, 8, 15, 24, 136, 264, 272, -16])
 def test_lora_rejects_bad_rank(r):
     assert _down(r=r, ldu=max(r, 8)) == cr.ERR_SHAPE
     assert _up(r=r, ldu=max(r, 8)) == cr.ERR_SHAPE
@@ -281,7 +281,7 @@ def test_linear_lora_validation():
     assert _fused(act=7) == cr.ERR_DTYPE
     lo = lambda **kw: [cr.ConvrotLora(**{**dict(u=FAKE, b=FAKE, ldu=32, rank=32), **kw})] * 3
     assert _fused(loras=lo(rank=24)) == cr.ERR_SHAPE
-    assert _fused(loras=lo(rank=144, ldu=144)) == cr.ERR_SHAPE
+    assert _fused(loras=lo(rank=272, ldu=272)) == cr.ERR_SHAPE
     assert _fused(loras=lo(ldu=16)) == cr.ERR_SHAPE            # ldu < rank
     assert _fused(loras=lo(ldu=36)) == cr.ERR_UNSUPPORTED
     assert _fused(loras=lo(u=None)) == cr.ERR_NULL

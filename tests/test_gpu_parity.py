@@ -680,6 +680,8 @@ def _check_lora(u_dev, y_dev, x64, ad, what):
     (1, 4096, 33, 80, "f32"),
     # long X: one workgroup per 128 rows (ragged M and K tails)
     (32760, 1040, 64, 64, "bf16"), (32900, 256, 50, 128, "f32"), (32769, 48, 40, 16, "bf16"),
+    # the largest ranks (long X with rank > 128 takes the 32 x 32 kernel)
+    (200, 1024, 300, 256, "bf16"), (32760, 256, 64, 192, "bf16"),
 ])
 def test_lora_parity(m, k, n, rank, dt):
     x, x64, ad = _lora_case(m, k, n, rank, dt, seed=m + rank)
@@ -756,6 +758,7 @@ def _fused_case(m, n_list, rank_list, k=3072, seed=21, gelu=False, g=256):
     (320, (1000, 700, 512), (64, 0, 16)),     # edge tiles, one weight without an adapter
     (512, (3072, 3072, 3072), (32, 48, 128)),  # interior tiles, every rank batch shape
     (1100, (9000,), (64,)),                    # several tiles per workgroup
+    (300, (700, 500), (256, 176)),             # the largest ranks
 ])
 def test_linear_lora_fused(m, ns, ranks):
     _say(f"fused lora m={m} n={ns} r={ranks}")
