@@ -181,6 +181,20 @@ def all_configs(args):
                 emit(workload=w.name, kernel="linear_grouped", n=n_total, m=m, k=k, group_size=g,
                      us=round(t * 1e3, 2), tops=round(tops, 1), mfma_frac=round(tops / PEAK_INT8_TOPS, 4))
                 del ys
+                # The same weights as one [n_total, k] matrix (codes and scales
+                # are per output row, so stacking the rows is the quantised
+                # concatenation), one plain launch.
+                if len({q.q.shape[1] for q in qws}) == 1 and all(q.bias is not None for q in qws):
+                    qcat = cr.QuantizedWeights(torch.cat([q.q for q in qws]),
+                                               torch.cat([q.scale for q in qws]),
+                                               torch.cat([q.bias for q in qws]), g)
+                    ycat = torch.empty((m, n_total), dtype=torch.float32, device="cuda")
+                    t = _time_ms(lambda: cr.linear(packed, qcat, out=ycat))
+                    tops = 2.0 * m * n_total * k / (t * 1e-3) / 1e12
+                    emit(workload=w.name, kernel="linear_concat", n=n_total, m=m, k=k, group_size=g,
+                         us=round(t * 1e3, 2), tops=round(tops, 1),
+                         mfma_frac=round(tops / PEAK_INT8_TOPS, 4))
+                    del qcat, ycat
             # Rank-64 low-rank adapters on the workload's linears (the first,
             # GELU one for the MLP): the down projection of each adapter into
             # one shared U buffer, and the linears with U B^T added in the

@@ -20,8 +20,9 @@
 // Operands are staged through LDS by direct-to-LDS loads of whole 128-byte
 // lines, swizzled like the persistent kernel's stages (chunk c of row r at
 // slot c ^ (r & 7) ^ ((r >> 3) & 1)), double-buffered (the next step's lines
-// load while this step's MFMAs run; a third stage measured no faster) with
-// one barrier per 128-byte K step.  Rows past M or n and bytes past K read
+// load while this step's MFMAs run; three, four or six stages measured no
+// faster on any short output, so the step is not waiting on load latency)
+// with one barrier per 128-byte K step.  Rows past M or n and bytes past K read
 // as zero.
 #include <algorithm>
 

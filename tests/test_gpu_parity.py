@@ -383,6 +383,12 @@ def test_linear_grouped_parity(rows, ns):
     # one launch per weight gives bit-identical outputs
     for i, q in enumerate(qws):
         assert torch.equal(cr.linear(p, q), ys[i])
+    # so does one launch on the weights stacked into one matrix (codes and
+    # scales are per output row; a missing bias is a zero bias)
+    qcat = cr.QuantizedWeights(
+        torch.cat([q.q for q in qws]), torch.cat([q.scale for q in qws]),
+        torch.cat([q.bias if q.bias is not None else torch.zeros_like(q.scale) for q in qws]), g)
+    assert torch.equal(cr.linear(p, qcat), torch.cat(ys, dim=1))
 
 
 @pytest.mark.parametrize("m,n,gelu", [(1100, 9000, False), (1300, 6500, True)])
