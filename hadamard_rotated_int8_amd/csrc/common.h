@@ -92,26 +92,27 @@ CR_DEVICE float div_by_recip(float x, float b, float r) {
 
 CR_DEVICE int clamp127(int q) { return max(-127, min(127, q)); }
 
-// erf(x) by Abramowitz & Stegun, Handbook of Mathematical Functions,
-// formula 7.1.26: for a >= 0, erf(a) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) e^{-a^2}
-// with t = 1 / (1 + p a), absolute error at most 1.5e-7; erf is odd.  About
-// a dozen VALU operations (hardware reciprocal and base-2 exponential)
-// instead of the device library's longer branch-and-select sequence, which
-// matters because the epilogue evaluates it for every output.
-CR_DEVICE float erf_as(float x) {
-  const float a = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, a, 1.0f));
-  float poly = __builtin_fmaf(t, 1.061405429f, -1.453152027f);
-  poly = __builtin_fmaf(t, poly, 1.421413741f);
-  poly = __builtin_fmaf(t, poly, -0.284496736f);
-  poly = __builtin_fmaf(t, poly, 0.254829592f);
-  poly *= t;
-  const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * a * a);  // e^{-a^2}
-  const float r = __builtin_fmaf(-poly, e, 1.0f);
-  return __builtin_copysignf(r, x);
+// GELU in its erf form, y Phi(y), with Phi the standard normal CDF.  For
+// either sign of y, y Phi(y) = max(y, 0) - |y| h with h = Phi(-|y|) =
+// erfc(|y| / sqrt 2) / 2.  h comes from Abramowitz & Stegun, Handbook of
+// Mathematical Functions, formula 7.1.26: for a >= 0,
+// erfc(a) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) e^{-a^2}, t = 1 / (1 + p a),
+// absolute error at most 1.5e-7.  The halving is folded into the
+// coefficients and 1/sqrt 2 into p and the exponent, which leaves eleven
+// full-rate operations plus the hardware reciprocal and base-2 exponential
+// per value (the form 0.5 y (1 + erf(y / sqrt 2)) takes three more).  The
+// GEMM epilogue evaluates it for every output, where each vector
+// instruction takes issue time from the matrix core.
+CR_DEVICE float gelu_erf(float y) {
+  const float a = fabsf(y);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.23164188826636f, a, 1.0f));  // p / sqrt 2
+  float q = __builtin_fmaf(t, 0.5307027145f, -0.7265760135f);  // a5 / 2, a4 / 2
+  q = __builtin_fmaf(t, q, 0.7107068705f);                     // a3 / 2
+  q = __builtin_fmaf(t, q, -0.142248368f);                     // a2 / 2
+  q = __builtin_fmaf(t, q, 0.127414796f);                      // a1 / 2
+  q *= t;
+  const float e = __builtin_amdgcn_exp2f(-0.72134752044448f * y * y);  // e^{-y^2 / 2}
+  return __builtin_fmaf(-a, q * e, fmaxf(y, 0.0f));
 }
-
-// GELU, the erf form x * Phi(x) = x/2 (1 + erf(x / sqrt 2)).
-CR_DEVICE float gelu_erf(float y) { return 0.5f * y * (1.0f + erf_as(y * 0.70710678118654752f)); }
 
 }  // namespace convrot
