@@ -116,6 +116,13 @@ convrot_status run_linear(const convrot_packed* x, const convrot_weights* const*
     }
     if (w[i]->n > 0) ++a.count;  // empty weights launch nothing
   }
+  // Adapters of rank 0 add nothing: with no adapter of higher rank the launch
+  // is the plain one (same values bit for bit, and the short-output path
+  // stays available).
+  if (a.lora) {
+    a.lora = false;
+    for (int i = 0; i < a.count; ++i) a.lora = a.lora || a.w[i].rank > 0;
+  }
   if (x->m == 0 || a.count == 0) return CONVROT_OK;
   if (!x->q) return CONVROT_ERR_NULL;
   if (y_dtype == CONVROT_F32 && !x->scale) return CONVROT_ERR_NULL;

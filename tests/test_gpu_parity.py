@@ -820,17 +820,26 @@ def test_linear_lora_full_size_sampled(name):
 
 
 def test_linear_lora_rank_zero_matches_plain_linear():
-    """With no adapter the fused path's values equal the plain linear's bit for bit
-    (the same float32 expression A s_x s_w + b, evaluated at the tile end)."""
+    """Weights without an adapter get the plain linear's values bit for bit:
+    when no weight of the launch has one (the plain launch), and next to a
+    weight that has one (the same float32 expression A s_x s_w + b, then
+    evaluated at the tile end)."""
     inp = wl.generate(wl.QKV, m=300, n_limit=900)
     g = 256
-    p = cr.pack_activations(dev(inp["x"]), g)
+    x = dev(inp["x"])
+    p = cr.pack_activations(x, g)
     ws = [_prep(wt, b, g) for wt, b in zip(inp["weights"], inp["biases"])]
     _say("fused lora rank 0")
     y_plain = cr.linear_grouped(p, ws)
     y_fused = cr.linear_lora(p, ws, [None] * len(ws))
     for a, b in zip(y_plain, y_fused):
         assert torch.equal(a, b)
+    _say("fused lora rank 0 beside rank 32")
+    ad = wl.lora_adapter(wl.QKV.k, ws[1].q.shape[0], 32, m=0, seed=5)
+    u = cr.lora_down(x, dev(ad["a"]), ad["scale"])
+    y_mixed = cr.linear_lora(p, ws, [None, (u, dev(ad["b"])), None])
+    assert torch.equal(y_mixed[0], y_plain[0]) and torch.equal(y_mixed[2], y_plain[2])
+    assert not torch.equal(y_mixed[1], y_plain[1])
 
 
 def test_lora_on_convrot_output():
