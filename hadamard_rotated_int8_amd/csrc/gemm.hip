@@ -807,8 +807,9 @@ int device_cu_count() {
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
-  int slices = 0;
-  if (gemm_split_wanted(a, device_cu_count(), &slices)) return launch_gemm_split(a, slices, stream);
+  int slices = 0, tile_n = 0;
+  if (gemm_split_wanted(a, device_cu_count(), &slices, &tile_n))
+    return launch_gemm_split(a, slices, tile_n, stream);
   GemmParams p{};
   p.qx = a.qx;
   p.sx = a.sx;

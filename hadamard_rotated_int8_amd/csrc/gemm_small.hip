@@ -5,8 +5,9 @@
 //   A[r, o] = sum_i Q_x[r, i] Q_w[o, i]   (int32),  Y = A s_x[r] s_w[o] + b[o].
 // The persistent kernel's 256 x 192 tiles leave most of the 256 CUs idle
 // when M is a few hundred rows (a 256 x 4096 x 4096 linear has 22 tiles).
-// Here the output is cut into 64 x 128 tiles and K into equal slices, so
-// that there is about one work item per CU:
+// Here the output is cut into 64 x 128 tiles (64 x 64 when that still gives
+// no more work items than CUs) and K into equal slices, so that there is
+// about one work item per CU:
 //   1. zero_kernel clears Y (viewed as int32);
 //   2. gemm_split_kernel computes one tile over one K slice and adds its
 //      int32 partial sums into Y with atomic adds.  Integer addition is exact
@@ -36,15 +37,22 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kSM = 64;                 // tile rows (Q_x)
-constexpr int kSN = 128;                // tile columns (Q_w rows)
 constexpr int kSK = 128;                // K bytes per step
 constexpr int kSStages = 2;
 constexpr int kXBytes = kSM * kSK;      // 8 KB
-constexpr int kStage = kXBytes + kSN * kSK;  // + 16 KB
-constexpr int kPieces = kStage / 1024;  // 1 KB direct-to-LDS loads per stage
-constexpr int kLoadsPerWave = kPieces / 4;
-static_assert(kPieces % 4 == 0, "pieces split evenly over 4 waves");
-static_assert((kSStages - 2) * kLoadsPerWave <= kVmMax, "vmcnt range");
+
+// Tile columns (Q_w rows) SN = 128, or 64 when the wider tiles would leave
+// most CUs idle.
+template <int SN>
+struct SplitCfg {
+  static constexpr int kStage = kXBytes + SN * kSK;   // + 8 or 16 KB
+  static constexpr int kPieces = kStage / 1024;       // 1 KB direct-to-LDS loads per stage
+  static constexpr int kLoadsPerWave = kPieces / 4;
+  static constexpr int kFN = SN / 64;                 // 32 x 32 blocks per wave
+  static_assert(SN == 64 || SN == 128, "tile columns");
+  static_assert(kPieces % 4 == 0, "pieces split evenly over 4 waves");
+  static_assert((kSStages - 2) * kLoadsPerWave <= kVmMax, "vmcnt range");
+};
 
 struct SplitSeg {
   const int8_t* qw;
@@ -73,8 +81,10 @@ CR_DEVICE int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 // an L2.
 // MODE 0: add int32 partial sums atomically; one slice only: 1 stores float32
 // A s_x s_w + b, 2 the same through GELU, 3 the int32 A.
-template <int MODE>
+template <int MODE, int SN>
 __global__ __launch_bounds__(256) void gemm_split_kernel(const SplitParams p) {
+  using C = SplitCfg<SN>;
+  constexpr int kStage = C::kStage, kLoadsPerWave = C::kLoadsPerWave, kFN = C::kFN;
   __shared__ __attribute__((aligned(1024))) int8_t smem[kSStages * kStage];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int item = xcd_slot(blockIdx.x, gridDim.x);
@@ -87,10 +97,10 @@ __global__ __launch_bounds__(256) void gemm_split_kernel(const SplitParams p) {
   const int rest = local / p.tiles_m;
   const int slice = rest % p.slices;
   const int tn = rest / p.slices;
-  const int m0 = tm * kSM, n0 = tn * kSN;
+  const int m0 = tm * kSM, n0 = tn * SN;
   const int K = p.K;
   const int rows = p.M - m0 < kSM ? p.M - m0 : kSM;
-  const int cols = sg.n - n0 < kSN ? sg.n - n0 : kSN;
+  const int cols = sg.n - n0 < SN ? sg.n - n0 : SN;
   const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(p.qx + (int64_t)m0 * K, rows * K);
   const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(sg.qw + (int64_t)n0 * K, cols * K);
   const int kb0 = slice * p.steps * kSK;  // first K byte of the slice
@@ -116,12 +126,12 @@ __global__ __launch_bounds__(256) void gemm_split_kernel(const SplitParams p) {
   };
 
   // Wave (wm, wn) = (wave / 2, wave % 2) owns rows 32 wm .. +31 and columns
-  // 64 wn .. +63 of the tile: two 32 x 32 accumulator blocks.  Lane l reads
-  // row l % 32 of a block, 16-byte chunk 2 kk + l / 32 of the step's K
-  // slice kk.
+  // (SN / 2) wn .. + SN / 2 - 1 of the tile: SN / 64 blocks of 32 x 32
+  // accumulators.  Lane l reads row l % 32 of a block, 16-byte chunk
+  // 2 kk + l / 32 of the step's K slice kk.
   const int wm = wave >> 1, wn = wave & 1;
   const int fr = lane & 31, fh = lane >> 5;
-  v16i acc[2] = {v16i{}, v16i{}};
+  v16i acc[kFN] = {};
 #pragma unroll
   for (int t = 0; t < kSStages - 1; ++t) issue(t);
   for (int t = 0; t < p.steps; ++t) {
@@ -137,8 +147,8 @@ __global__ __launch_bounds__(256) void gemm_split_kernel(const SplitParams p) {
       const int xrow = wm * 32 + fr;
       const v4i xf = *reinterpret_cast<const v4i*>(st + xrow * kSK + (((2 * kk + fh) ^ swz(xrow)) << 4));
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int wrow = wn * 64 + j * 32 + fr;
+      for (int j = 0; j < kFN; ++j) {
+        const int wrow = wn * (SN / 2) + j * 32 + fr;
         const v4i wf = *reinterpret_cast<const v4i*>(st + kXBytes + wrow * kSK +
                                                      (((2 * kk + fh) ^ swz(wrow)) << 4));
         acc[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf, wf, acc[j], 0, 0, 0);
@@ -149,8 +159,8 @@ __global__ __launch_bounds__(256) void gemm_split_kernel(const SplitParams p) {
   // Accumulator register i of lane l: row 8 (i / 4) + 4 (l / 32) + i % 4,
   // column l % 32 of the block.
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = n0 + wn * 64 + j * 32 + fr;
+  for (int j = 0; j < kFN; ++j) {
+    const int col = n0 + wn * (SN / 2) + j * 32 + fr;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int row = m0 + wm * 32 + 8 * (i / 4) + 4 * fh + (i & 3);
@@ -212,18 +222,21 @@ dim3 elementwise_grid(int64_t m, int64_t n) {
 // loads sustain here; one slice with direct stores about 3 us + 0.6 us per
 // K step and round of 64 x 128 tiles.  The cheaper split form is taken when
 // it is estimated 15 % faster than the persistent kernel, only while that
-// kernel has fewer tiles than CUs.
-bool gemm_split_wanted(const GemmArgs& a, int cus, int* slices) {
+// kernel has fewer tiles than CUs.  A single slice whose 64 x 64 tiles still
+// fit the CUs uses those: twice the work items, each reading 16 KB per K
+// step instead of 24 (256 x 4096 x 4096: 14.2 us instead of 20.5).
+bool gemm_split_wanted(const GemmArgs& a, int cus, int* slices, int* tile_n) {
   if (a.lora) return false;
   const int64_t steps = (a.k + kSK - 1) / kSK;
-  int64_t big = 0, small = 0;
+  int64_t big = 0, small = 0, narrow = 0;
   for (int i = 0; i < a.count; ++i) {
     big += ((a.m + 255) / 256) * ((a.w[i].n + 191) / 192);
-    small += ((a.m + kSM - 1) / kSM) * ((a.w[i].n + kSN - 1) / kSN);
+    small += ((a.m + kSM - 1) / kSM) * ((a.w[i].n + 127) / 128);
+    narrow += ((a.m + kSM - 1) / kSM) * ((a.w[i].n + 63) / 64);
   }
   if (big >= cus || steps < 2) return false;
   const double main_us = 3.0 + 1.2 * double(steps);
-  const double atomic_us = 8.0 + double(small) * double(steps) * kStage / 6.5e6;
+  const double atomic_us = 8.0 + double(small) * double(steps) * SplitCfg<128>::kStage / 6.5e6;
   const double direct_us = 3.0 + 0.6 * double(steps) * double((small + cus - 1) / cus);
   if (!(std::min(atomic_us, direct_us) < 0.85 * main_us)) return false;
   // About one work item per CU (measured 10-15 % faster than two: fewer
@@ -233,10 +246,14 @@ bool gemm_split_wanted(const GemmArgs& a, int cus, int* slices) {
   if (s > steps / 2) s = steps / 2;
   if (s < 1 || direct_us <= atomic_us) s = 1;
   *slices = int(s);
+  *tile_n = (s == 1 && narrow <= cus) ? 64 : 128;
   return true;
 }
 
-hipError_t launch_gemm_split(const GemmArgs& a, int slices, hipStream_t stream) {
+namespace {
+
+template <int SN>
+hipError_t launch_split_t(const GemmArgs& a, int slices, hipStream_t stream) {
   SplitParams p{};
   p.qx = a.qx;
   p.sx = a.sx;
@@ -258,7 +275,7 @@ hipError_t launch_gemm_split(const GemmArgs& a, int slices, hipStream_t stream) 
     sg.acc = static_cast<int*>(a.w[i].y);
     sg.ld = a.w[i].ldy;
     sg.n = int(a.w[i].n);
-    sg.tiles_n = (sg.n + kSN - 1) / kSN;
+    sg.tiles_n = (sg.n + SN - 1) / SN;
     sg.item0 = items;
     items += sg.tiles_n * p.slices * p.tiles_m;
     if (!direct)
@@ -267,13 +284,13 @@ hipError_t launch_gemm_split(const GemmArgs& a, int slices, hipStream_t stream) 
   }
   const dim3 grid(static_cast<unsigned>(items));
   if (!direct)
-    hipLaunchKernelGGL(gemm_split_kernel<0>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gemm_split_kernel<0, SN>), grid, dim3(256), 0, stream, p);
   else if (a.raw_i32)
-    hipLaunchKernelGGL(gemm_split_kernel<3>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gemm_split_kernel<3, SN>), grid, dim3(256), 0, stream, p);
   else if (a.gelu)
-    hipLaunchKernelGGL(gemm_split_kernel<2>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gemm_split_kernel<2, SN>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL(gemm_split_kernel<1>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gemm_split_kernel<1, SN>), grid, dim3(256), 0, stream, p);
   if (!direct && !a.raw_i32) {
     for (int i = 0; i < a.count; ++i) {
       float* y = static_cast<float*>(a.w[i].y);
@@ -287,6 +304,14 @@ hipError_t launch_gemm_split(const GemmArgs& a, int slices, hipStream_t stream) 
     }
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_split(const GemmArgs& a, int slices, int tile_n, hipStream_t stream) {
+  if (tile_n == 64) return launch_split_t<64>(a, slices, stream);
+  if (tile_n == 128) return launch_split_t<128>(a, slices, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace convrot

@@ -50,10 +50,11 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 // Outputs with few 256 x 192 tiles (short M or narrow N, no adapters): the
-// split-K path (64 x 128 tiles, int32 atomic sums into Y, then the scaling
-// pass).  gemm_split_wanted decides and picks the number of K slices.
-bool gemm_split_wanted(const GemmArgs& a, int cus, int* slices);
-hipError_t launch_gemm_split(const GemmArgs& a, int slices, hipStream_t stream);
+// split-K path (64 x 128 or 64 x 64 tiles; with several K slices int32
+// atomic sums into Y, then the scaling pass).  gemm_split_wanted decides and
+// picks the number of K slices and the tile width (64 or 128).
+bool gemm_split_wanted(const GemmArgs& a, int cus, int* slices, int* tile_n);
+hipError_t launch_gemm_split(const GemmArgs& a, int slices, int tile_n, hipStream_t stream);
 
 constexpr int kLoraMaxRank = 256;        // adapter ranks 16, 32, ..., 256
 constexpr int64_t kLoraMaxLdu = 1 << 20;  // U row stride limit (32-bit buffer offsets)

@@ -496,6 +496,32 @@ def test_linear_gelu_short_output(m, n):
     check_y(y, y_or, sx_or, sw_or, 1024, gelu=True, what=f"gelu short {m}x{n}")
 
 
+@pytest.mark.parametrize("m,k,n", [(200, 1040, 4000),    # 64 x 64 tiles, ragged M, N and K
+                                   (512, 1040, 3000)])   # 64 x 128 tiles
+def test_linear_short_output_tile_widths(m, k, n):
+    """The split path's single-slice form at both tile widths: raw int32 A
+    bit-exact, float32 Y and GELU(Y) within the oracle bounds."""
+    rng = np.random.default_rng(m + n)
+    g = 16
+    x = (rng.standard_normal((m, k)) * 0.5).astype(np.float32)
+    wt = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    b = (rng.standard_normal(n) * 0.01).astype(np.float32)
+    _say(f"linear short output tile widths m={m} k={k} n={n}")
+    p = cr.pack_activations(dev(x), g)
+    qw = _prep(wt, b, g)
+    qx_or, sx_or = orc.pack_activations(x.astype(np.float64), g)
+    qw_or, sw_or = orc.quantize_weights(wt, g)
+    # the device's int32 product of the oracle's codes
+    p_or = cr.PackedActivation(dev(qx_or.astype(np.int8)), dev(sx_or.astype(np.float32)), g)
+    a = host(cr.linear(p_or, qw, raw_i32=True)).astype(np.int64)
+    assert np.array_equal(a, orc.int_gemm(qx_or, qw_or))
+    y = host(cr.linear(p, qw))
+    check_y(y, orc.linear(qx_or, sx_or, qw_or, sw_or, b), sx_or, sw_or, k, what=f"short {m}x{n}")
+    yg = host(cr.linear(p, qw, gelu=True))
+    check_y(yg, orc.linear(qx_or, sx_or, qw_or, sw_or, b, act="gelu"), sx_or, sw_or, k,
+            gelu=True, what=f"short gelu {m}x{n}")
+
+
 def test_mlp_pair():
     """DiT MLP: up (GELU fused) then down on the float32 GELU output."""
     w = wl.MLP
