@@ -21,10 +21,10 @@
 // Operands are staged through LDS by direct-to-LDS loads of whole 128-byte
 // lines, swizzled like the persistent kernel's stages (chunk c of row r at
 // slot c ^ (r & 7) ^ ((r >> 3) & 1)), double-buffered (the next step's lines
-// load while this step's MFMAs run; three, four or six stages measured no
-// faster on any short output, so the step is not waiting on load latency)
-// with one barrier per 128-byte K step.  Rows past M or n and bytes past K read
-// as zero.
+// load while this step's MFMAs run) with one barrier per 128-byte K step.
+// Three, four or six stages measured no faster on any short output; a
+// second wave per SIMD did (see the wave layout below).  Rows past M or n
+// and bytes past K read as zero.
 #include <algorithm>
 
 #include "common.h"
