@@ -3,6 +3,7 @@
 // Every check runs on the host before any HIP call, so an invalid call
 // returns a status code and touches neither the GPU nor the HIP runtime.
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 #include "../../include/convrot.h"
 #include "kernels.h"
@@ -124,6 +125,12 @@ convrot_status run_linear(const convrot_packed* x, const convrot_weights* const*
     for (int i = 0; i < a.count; ++i) a.lora = a.lora || a.w[i].rank > 0;
   }
   if (x->m == 0 || a.count == 0) return CONVROT_OK;
+  // The persistent kernel numbers its 256 x 192 output tiles with 32-bit
+  // integers (no buffer that large can exist, but the count is checked
+  // rather than assumed).
+  int64_t tiles = 0;
+  for (int i = 0; i < a.count; ++i) tiles += (a.w[i].n + 191) / 192;
+  if (tiles * ((x->m + 255) / 256) > int64_t(INT32_MAX)) return CONVROT_ERR_SHAPE;
   if (!x->q) return CONVROT_ERR_NULL;
   if (y_dtype == CONVROT_F32 && !x->scale) return CONVROT_ERR_NULL;
   if (!aligned16(x->q)) return CONVROT_ERR_UNSUPPORTED;

@@ -138,6 +138,9 @@ def test_linear_validation():
     assert _lin(qw=FAKE + 1) == cr.ERR_UNSUPPORTED
     assert _lin(qx=FAKE + 8) == cr.ERR_UNSUPPORTED
     assert _lin(k=1040, gx=16, kw=1040, gw=16, qx=None) == cr.ERR_NULL  # ragged K is accepted
+    # each extent fits, but the number of 256 x 192 output tiles would not fit 32 bits
+    big = 2**31 - 1
+    assert _lin(m=big, n=big, ldy=big) == cr.ERR_SHAPE
 
 
 def test_linear_empty_is_a_no_op():
