@@ -233,6 +233,44 @@ class QuantizedWeights:
                               self.group_size)
 
 
+# The C ABI sees only pointers and sizes, so the extents, dtypes, layouts and
+# device of every tensor are checked here: a wrong one would otherwise make a
+# kernel read or write outside it.
+def _same_device(dev, *ts):
+    for t in ts:
+        if t is not None and t.device != dev:
+            raise ValueError("all tensors of one call must be on the same device")
+
+
+def _check_packed(x: PackedActivation) -> torch.device:
+    q, s = x.q, x.scale
+    _require_cuda(q, "the packed codes")
+    if q.dtype != torch.int8 or q.dim() != 2 or not q.is_contiguous():
+        raise ValueError("the packed codes must be a contiguous int8 [m, k] device tensor")
+    if s.dtype != torch.float32 or tuple(s.shape) != (q.shape[0],) or not s.is_contiguous():
+        raise ValueError("the packed scales must be a contiguous float32 [m] tensor")
+    _same_device(q.device, s)
+    return q.device
+
+
+def _check_weights(w: "QuantizedWeights", dev):
+    q = w.q
+    if q.dtype != torch.int8 or q.dim() != 2 or not q.is_contiguous():
+        raise ValueError("weight codes must be a contiguous int8 [n, k] tensor")
+    n = q.shape[0]
+    for t, what in ((w.scale, "weight scales"), (w.bias, "bias")):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (n,)
+                              or not t.is_contiguous()):
+            raise ValueError(f"the {what} must be a contiguous float32 [n] tensor")
+    _same_device(dev, q, w.scale, w.bias)
+
+
+def _check_out(o: torch.Tensor, m: int, n: int, dtype, dev):
+    if o.dtype != dtype or tuple(o.shape) != (m, n) or o.stride(1) != 1:
+        raise ValueError(f"an output must be a {dtype} [{m}, {n}] view with unit column stride")
+    _same_device(dev, o)
+
+
 def quantize_weights(w: torch.Tensor, group_size: int, bias: torch.Tensor | None = None
                      ) -> QuantizedWeights:
     """Offline W_rot = W R and per-row int8 codes (float32 W [n, k] on the device)."""
@@ -240,10 +278,15 @@ def quantize_weights(w: torch.Tensor, group_size: int, bias: torch.Tensor | None
     if w.dtype != torch.float32 or w.dim() != 2 or w.stride(1) != 1:
         raise ValueError("w must be a float32 [n, k] device tensor with unit column stride")
     n, k = w.shape
+    if bias is not None and (bias.dtype != torch.float32 or tuple(bias.shape) != (n,)
+                             or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous float32 [n] tensor")
+    _same_device(w.device, bias)
     q = torch.empty((n, k), dtype=torch.int8, device=w.device)
     s = torch.empty((n,), dtype=torch.float32, device=w.device)
-    st = convrot_quantize_weights(_ptr(w), n, k, w.stride(0), group_size, _ptr(q), _ptr(s),
-                                  _stream())
+    with torch.cuda.device(w.device):
+        st = convrot_quantize_weights(_ptr(w), n, k, w.stride(0), group_size, _ptr(q), _ptr(s),
+                                      _stream())
     if st != OK:
         raise ConvrotError(st, "convrot_quantize_weights")
     return QuantizedWeights(q, s, bias, group_size)
@@ -263,8 +306,11 @@ def pack_activations(x: torch.Tensor, group_size: int, out: PackedActivation | N
         out = PackedActivation(torch.empty((m, k), dtype=torch.int8, device=x.device),
                                torch.empty((m,), dtype=torch.float32, device=x.device),
                                group_size)
+    if tuple(out.q.shape) != (m, k) or _check_packed(out) != x.device:
+        raise ValueError("out must hold [m, k] codes and [m] scales on x's device")
     c = ConvrotPacked(_ptr(out.q), _ptr(out.scale), 0, 0, 0)
-    st = convrot_pack_activations(_ptr(x), dt, m, k, x.stride(0), group_size, c, _stream())
+    with torch.cuda.device(x.device):
+        st = convrot_pack_activations(_ptr(x), dt, m, k, x.stride(0), group_size, c, _stream())
     if st != OK:
         raise ConvrotError(st, "convrot_pack_activations")
     out.group_size = group_size
@@ -274,15 +320,17 @@ def pack_activations(x: torch.Tensor, group_size: int, out: PackedActivation | N
 def linear(x: PackedActivation, w: QuantizedWeights, out: torch.Tensor | None = None,
            raw_i32: bool = False, gelu: bool = False) -> torch.Tensor:
     """Y = (Q_x Q_w^T) s_x s_w + b (float32 [m, n]); raw_i32 returns the int32 A."""
+    dev = _check_packed(x)
+    _check_weights(w, dev)
     m = x.q.shape[0]
     n = w.q.shape[0]
     dtype = torch.int32 if raw_i32 else torch.float32
     if out is None:
-        out = torch.empty((m, n), dtype=dtype, device=x.q.device)
-    if out.dtype != dtype or out.dim() != 2 or out.stride(1) != 1:
-        raise ValueError("out has the wrong dtype or layout")
-    st = convrot_linear(x.as_c(), w.as_c(), _ptr(out), I32 if raw_i32 else F32, out.stride(0),
-                        ACT_GELU if gelu else ACT_NONE, _stream())
+        out = torch.empty((m, n), dtype=dtype, device=dev)
+    _check_out(out, m, n, dtype, dev)
+    with torch.cuda.device(dev):
+        st = convrot_linear(x.as_c(), w.as_c(), _ptr(out), I32 if raw_i32 else F32,
+                            out.stride(0), ACT_GELU if gelu else ACT_NONE, _stream())
     if st != OK:
         raise ConvrotError(st, "convrot_linear")
     return out
@@ -291,16 +339,21 @@ def linear(x: PackedActivation, w: QuantizedWeights, out: torch.Tensor | None = 
 def linear_grouped(x: PackedActivation, ws, outs=None, raw_i32: bool = False,
                    gelu: bool = False):
     """Several linears on one packed activation in one launch; returns the outputs."""
+    dev = _check_packed(x)
+    for w in ws:
+        _check_weights(w, dev)
     m = x.q.shape[0]
     dtype = torch.int32 if raw_i32 else torch.float32
     if outs is None:
-        outs = [torch.empty((m, w.q.shape[0]), dtype=dtype, device=x.q.device) for w in ws]
-    for o in outs:
-        if o.dtype != dtype or o.dim() != 2 or o.stride(1) != 1:
-            raise ValueError("an output has the wrong dtype or layout")
-    st = convrot_linear_grouped(x.as_c(), [w.as_c() for w in ws], [_ptr(o) for o in outs],
-                                [o.stride(0) for o in outs], I32 if raw_i32 else F32,
-                                ACT_GELU if gelu else ACT_NONE, _stream())
+        outs = [torch.empty((m, w.q.shape[0]), dtype=dtype, device=dev) for w in ws]
+    if len(outs) != len(ws):
+        raise ValueError("one output per weight")
+    for o, w in zip(outs, ws):
+        _check_out(o, m, w.q.shape[0], dtype, dev)
+    with torch.cuda.device(dev):
+        st = convrot_linear_grouped(x.as_c(), [w.as_c() for w in ws], [_ptr(o) for o in outs],
+                                    [o.stride(0) for o in outs], I32 if raw_i32 else F32,
+                                    ACT_GELU if gelu else ACT_NONE, _stream())
     if st != OK:
         raise ConvrotError(st, "convrot_linear_grouped")
     return outs
@@ -327,8 +380,10 @@ def lora_down(x: torch.Tensor, a: torch.Tensor, scale: float,
         out = torch.empty((m, rank), dtype=torch.bfloat16, device=x.device)
     if out.dtype != torch.bfloat16 or out.shape != (m, rank) or out.stride(1) != 1:
         raise ValueError("out must be a bfloat16 [m, rank] view with unit column stride")
-    st = convrot_lora_down(_ptr(x), dt, m, k, x.stride(0), _ptr(a), rank, float(scale), _ptr(out),
-                           out.stride(0), _stream())
+    _same_device(x.device, a, out)
+    with torch.cuda.device(x.device):
+        st = convrot_lora_down(_ptr(x), dt, m, k, x.stride(0), _ptr(a), rank, float(scale),
+                               _ptr(out), out.stride(0), _stream())
     if st != OK:
         raise ConvrotError(st, "convrot_lora_down")
     return out
@@ -341,6 +396,7 @@ def _check_u(u: torch.Tensor, m: int):
 
 def lora_up_add(u: torch.Tensor, b: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
     """y += U B^T in place (y float32 [m, n]), a separate pass; returns y."""
+    _require_cuda(y, "y")
     if y.dtype != torch.float32 or y.dim() != 2 or y.stride(1) != 1:
         raise ValueError("y must be a float32 [m, n] tensor with unit column stride")
     m, n = y.shape
@@ -348,8 +404,10 @@ def lora_up_add(u: torch.Tensor, b: torch.Tensor, y: torch.Tensor) -> torch.Tens
     rank = u.shape[1]
     if b.dtype != torch.bfloat16 or not b.is_contiguous() or b.shape != (n, rank):
         raise ValueError("b must be a contiguous bfloat16 [n, rank] tensor")
-    st = convrot_lora_up_add(_ptr(u), u.stride(0), _ptr(b), m, n, rank, _ptr(y), y.stride(0),
-                             _stream())
+    _same_device(y.device, u, b)
+    with torch.cuda.device(y.device):
+        st = convrot_lora_up_add(_ptr(u), u.stride(0), _ptr(b), m, n, rank, _ptr(y), y.stride(0),
+                                 _stream())
     if st != OK:
         raise ConvrotError(st, "convrot_lora_up_add")
     return y
@@ -362,11 +420,16 @@ def linear_lora(x: PackedActivation, ws, adapters, outs=None, gelu: bool = False
     [m, rank]), b bfloat16 [n, rank] -- or None for a weight without one.
     Returns the float32 outputs act(Y + U B^T).
     """
+    dev = _check_packed(x)
+    for w in ws:
+        _check_weights(w, dev)
     m = x.q.shape[0]
     if len(adapters) != len(ws):
         raise ValueError("one adapter (or None) per weight")
     if outs is None:
-        outs = [torch.empty((m, w.q.shape[0]), dtype=torch.float32, device=x.q.device) for w in ws]
+        outs = [torch.empty((m, w.q.shape[0]), dtype=torch.float32, device=dev) for w in ws]
+    if len(outs) != len(ws):
+        raise ValueError("one output per weight")
     loras = []
     for w, ad in zip(ws, adapters):
         if ad is None:
@@ -377,13 +440,14 @@ def linear_lora(x: PackedActivation, ws, adapters, outs=None, gelu: bool = False
         rank = u.shape[1]
         if b.dtype != torch.bfloat16 or not b.is_contiguous() or b.shape != (w.q.shape[0], rank):
             raise ValueError("b must be a contiguous bfloat16 [n, rank] tensor")
+        _same_device(dev, u, b)
         loras.append(ConvrotLora(_ptr(u), _ptr(b), u.stride(0), rank))
-    for o in outs:
-        if o.dtype != torch.float32 or o.dim() != 2 or o.stride(1) != 1:
-            raise ValueError("an output has the wrong dtype or layout")
-    st = convrot_linear_lora(x.as_c(), [w.as_c() for w in ws], loras, [_ptr(o) for o in outs],
-                             [o.stride(0) for o in outs], ACT_GELU if gelu else ACT_NONE,
-                             _stream())
+    for o, w in zip(outs, ws):
+        _check_out(o, m, w.q.shape[0], torch.float32, dev)
+    with torch.cuda.device(dev):
+        st = convrot_linear_lora(x.as_c(), [w.as_c() for w in ws], loras, [_ptr(o) for o in outs],
+                                 [o.stride(0) for o in outs], ACT_GELU if gelu else ACT_NONE,
+                                 _stream())
     if st != OK:
         raise ConvrotError(st, "convrot_linear_lora")
     return outs

@@ -555,6 +555,42 @@ def test_mlp_pair():
     check_y(y2, y_or, sh_or, sd_or, 12288, what="mlp chain")
 
 
+def test_helpers_reject_bad_tensors():
+    """The torch helpers check what the C ABI cannot see (extents, dtypes,
+    layouts) and raise before launching anything."""
+    g = 16
+    x = torch.randn(64, 256, device="cuda")
+    p = cr.pack_activations(x, g)
+    qw = cr.quantize_weights(torch.randn(32, 256, device="cuda") * 0.02, g,
+                             torch.zeros(32, device="cuda"))
+    bf = torch.bfloat16
+    bad = [
+        lambda: cr.linear(p, qw, out=torch.empty(63, 32, device="cuda")),   # too few rows
+        lambda: cr.linear(p, qw, out=torch.empty(64, 31, device="cuda")),   # too few columns
+        lambda: cr.linear(p, qw, out=torch.empty(64, 32, dtype=torch.int32, device="cuda")),
+        lambda: cr.quantize_weights(torch.randn(32, 256, device="cuda"), g,
+                                    torch.zeros(31, device="cuda")),        # bias length
+        lambda: cr.quantize_weights(torch.randn(32, 256, device="cuda"), g,
+                                    torch.zeros(32, dtype=torch.float64, device="cuda")),
+        lambda: cr.linear(p, cr.QuantizedWeights(qw.q, qw.scale[:16], qw.bias, g)),
+        lambda: cr.linear(cr.PackedActivation(p.q, p.scale[:10], g), qw),
+        lambda: cr.linear(cr.PackedActivation(p.q[:, ::2], p.scale, g), qw),  # strided codes
+        lambda: cr.linear_grouped(p, [qw, qw], outs=[torch.empty(64, 32, device="cuda")]),
+        lambda: cr.pack_activations(x, g, out=cr.PackedActivation(
+            torch.empty(64, 128, dtype=torch.int8, device="cuda"), torch.empty(64, device="cuda"), g)),
+        lambda: cr.linear_lora(p, [qw], [(torch.empty(63, 16, dtype=bf, device="cuda"),
+                                          torch.empty(32, 16, dtype=bf, device="cuda"))]),
+        lambda: cr.lora_up_add(torch.empty(64, 16, dtype=bf, device="cuda"),
+                               torch.empty(32, 16, dtype=bf, device="cuda"),
+                               torch.empty(64, 32)),                        # host y
+    ]
+    _say("helpers reject bad tensors")
+    for i, call in enumerate(bad):
+        with pytest.raises(ValueError):
+            call()
+    assert cr.linear(p, qw).shape == (64, 32)  # the correct call still runs
+
+
 def test_empty_inputs():
     x = torch.empty((0, 1024), dtype=torch.bfloat16, device="cuda")
     p = cr.pack_activations(x, 256)
