@@ -555,6 +555,70 @@ def test_mlp_pair():
     check_y(y2, y_or, sh_or, sd_or, 12288, what="mlp chain")
 
 
+def _random_case(rng, large):
+    """A valid linear problem of random shape, small enough for the oracle:
+    K a multiple of 16 up to 4096, M up to 600 and one to three weights of up
+    to 1200 rows (M * sum(N) * K <= 2e8: mostly the short-output path); or
+    (large) K a multiple of 16 up to 128, M 1000..3000 and weights of
+    500..4000 rows (at most 1.2e9 products: the persistent kernel with many
+    ragged tiles and its zero-padded K steps).  G is a power of four
+    dividing K."""
+    while True:
+        if large:
+            k = 16 * int(rng.integers(1, 9))
+            m = int(rng.integers(1000, 3001))
+            ns = [int(rng.integers(500, 4001)) for _ in range(int(rng.integers(1, 4)))]
+        else:
+            k = 16 * int(rng.integers(1, 257))
+            m = int(rng.integers(1, 601))
+            ns = [int(rng.integers(1, 1201)) for _ in range(int(rng.integers(1, 4)))]
+        gs = [4 ** n for n in range(8) if 4 ** n <= k and k % (4 ** n) == 0]
+        g = int(rng.choice(gs))
+        if m * sum(ns) * k <= (1.2e9 if large else 2e8):
+            return m, k, g, ns
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes(seed):
+    """Seeded random shapes through the pack and the grouped linear (raw
+    int32, float32 or GELU output), against the oracle: ragged M, N and K,
+    every group size, both GEMM paths and their tile widths."""
+    rng = np.random.default_rng(1000 + seed)
+    m, k, g, ns = _random_case(rng, large=seed % 3 == 2)
+    out = ("raw", "f32", "gelu")[(seed // 3) % 3]
+    xdt = "bf16" if seed % 2 else "f32"
+    x32 = rng.standard_normal((m, k)).astype(np.float32)
+    x32[:, rng.choice(k, max(1, k // 200), replace=False)] *= 20
+    if xdt == "bf16":
+        xt = torch.from_numpy(x32).to(torch.bfloat16)
+        x64 = xt.to(torch.float64).numpy()
+    else:
+        xt = torch.from_numpy(x32)
+        x64 = x32.astype(np.float64)
+    wts = [(rng.standard_normal((n, k)) * 0.02).astype(np.float32) for n in ns]
+    bs = [(rng.standard_normal(n) * 0.01).astype(np.float32) if i != 1 else None
+          for i, n in enumerate(ns)]
+    _say(f"random shapes seed={seed}: m={m} k={k} G={g} n={ns} {xdt} {out}")
+    p = cr.pack_activations(xt.cuda(), g)
+    qx_or, sx_or = orc.pack_activations(x64, g)
+    check_pack(host(p.q), host(p.scale), qx_or, sx_or, f"seed {seed}")
+    qws = [_prep(wt, b, g) for wt, b in zip(wts, bs)]
+    ors = [orc.quantize_weights(wt, g) for wt in wts]
+    for qw, (qw_or, sw_or) in zip(qws, ors):
+        assert np.array_equal(host(qw.q), qw_or) and np.array_equal(host(qw.scale), sw_or)
+    if out == "raw":
+        p_or = cr.PackedActivation(dev(qx_or.astype(np.int8)), dev(sx_or.astype(np.float32)), g)
+        ys = cr.linear_grouped(p_or, qws, raw_i32=True)
+        for y, (qw_or, _) in zip(ys, ors):
+            assert np.array_equal(host(y).astype(np.int64), orc.int_gemm(qx_or, qw_or))
+    else:
+        gelu = out == "gelu"
+        ys = cr.linear_grouped(p, qws, gelu=gelu)
+        for i, (y, (qw_or, sw_or), b) in enumerate(zip(ys, ors, bs)):
+            y_or = orc.linear(qx_or, sx_or, qw_or, sw_or, b, act="gelu" if gelu else None)
+            check_y(host(y), y_or, sx_or, sw_or, k, gelu=gelu, what=f"seed {seed} w{i}")
+
+
 def test_helpers_reject_bad_tensors():
     """The torch helpers check what the C ABI cannot see (extents, dtypes,
     layouts) and raise before launching anything."""
