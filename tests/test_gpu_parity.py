@@ -900,6 +900,20 @@ def test_linear_lora_fused(m, ns, ranks):
     _fused_case(m, ns, ranks)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_linear_lora_fused_random(seed):
+    """Seeded random shapes and ranks (0 = no adapter) for the fused path."""
+    rng = np.random.default_rng(2000 + seed)
+    m = int(rng.integers(1, 701))
+    k = 256 * int(rng.integers(1, 17))
+    cnt = int(rng.integers(1, 4))
+    ns = tuple(int(rng.integers(1, 1501)) for _ in range(cnt))
+    ranks = tuple(int(16 * rng.integers(0, 17)) for _ in range(cnt))
+    gelu = bool(seed % 2)
+    _say(f"fused lora random seed={seed}: m={m} k={k} n={ns} r={ranks} gelu={gelu}")
+    _fused_case(m, ns, ranks, k=k, seed=30 + seed, gelu=gelu)
+
+
 def test_linear_lora_fused_gelu_and_short_k():
     _say("fused lora gelu, k=512")
     _fused_case(300, (1300,), (64,), k=512, gelu=True)
