@@ -385,15 +385,20 @@ hipError_t launch_down_rows(const void* x, int64_t ldx, int m, int k, const uint
 template <typename InT>
 hipError_t launch_down(const void* x, int64_t ldx, int m, int k, const uint16_t* a, int r,
                        float scale, uint16_t* u, int64_t ldu, hipStream_t stream) {
-  // Long X (a 128-row block for every CU) and rank <= 128: one workgroup per
-  // 128 rows and all of U's columns.  Otherwise 32 x 32 blocks of U, K split
-  // over waves (any rank).
-  if ((m + 127) / 128 >= device_cu_count() && r <= 128) {
+  // Long X (a 128-row block for every CU): one workgroup per 128 rows and all
+  // of U's columns (up to 8 blocks of 32: 128 accumulator registers per
+  // lane; a bf16 stage is 48 KB, a float32 one 64 KB).  Otherwise 32 x 32
+  // blocks of U, K split over waves.
+  if ((m + 127) / 128 >= device_cu_count()) {
     switch ((r + 31) / 32) {
       case 1: return launch_down_rows<InT, 1>(x, ldx, m, k, a, r, scale, u, ldu, stream);
       case 2: return launch_down_rows<InT, 2>(x, ldx, m, k, a, r, scale, u, ldu, stream);
       case 3: return launch_down_rows<InT, 3>(x, ldx, m, k, a, r, scale, u, ldu, stream);
       case 4: return launch_down_rows<InT, 4>(x, ldx, m, k, a, r, scale, u, ldu, stream);
+      case 5: return launch_down_rows<InT, 5>(x, ldx, m, k, a, r, scale, u, ldu, stream);
+      case 6: return launch_down_rows<InT, 6>(x, ldx, m, k, a, r, scale, u, ldu, stream);
+      case 7: return launch_down_rows<InT, 7>(x, ldx, m, k, a, r, scale, u, ldu, stream);
+      case 8: return launch_down_rows<InT, 8>(x, ldx, m, k, a, r, scale, u, ldu, stream);
       default: return hipErrorInvalidValue;
     }
   }
@@ -405,7 +410,8 @@ hipError_t launch_down(const void* x, int64_t ldx, int m, int k, const uint16_t*
                      static_cast<const InT*>(x), ldx, m, k, a, r, scale, u, ldu, ncb);
   return hipGetLastError();
 }
-static_assert(kLoraMaxRank % 16 == 0, "ranks are multiples of 16");
+static_assert(kLoraMaxRank % 16 == 0 && kLoraMaxRank <= 8 * 32,
+              "ranks are multiples of 16, at most 8 blocks of 32 U columns");
 
 }  // namespace
 

@@ -815,8 +815,10 @@ def _check_lora(u_dev, y_dev, x64, ad, what):
     (1, 4096, 33, 80, "f32"),
     # long X: one workgroup per 128 rows (ragged M and K tails)
     (32760, 1040, 64, 64, "bf16"), (32900, 256, 50, 128, "f32"), (32769, 48, 40, 16, "bf16"),
-    # the largest ranks (long X with rank > 128 takes the 32 x 32 kernel)
+    # the largest ranks: short X (32 x 32 kernel), long X (up to 8 column
+    # blocks per 128-row workgroup; ragged M and K)
     (200, 1024, 300, 256, "bf16"), (32760, 256, 64, 192, "bf16"),
+    (32800, 1040, 64, 224, "bf16"), (32761, 512, 40, 256, "f32"),
 ])
 def test_lora_parity(m, k, n, rank, dt):
     x, x64, ad = _lora_case(m, k, n, rank, dt, seed=m + rank)
