@@ -217,6 +217,15 @@ def all_configs(args):
                 emit(workload=w.name, kernel="lora_down", m=m, k=k, rank=rank, adapters=len(ads),
                      us=round(td * 1e3, 2),
                      x_gbps=round(len(ads) * m * k * xb / (td * 1e-3) / 1e9, 1))
+                # Adapters that share a scale can stack their A matrices into one
+                # down projection that reads X once and fills the same U buffer.
+                if len(ads) > 1 and len({ad["scale"] for ad in ads}) == 1:
+                    a_cat = torch.cat(a_dev)
+                    tds = _time_ms(lambda: cr.lora_down(x, a_cat, ads[0]["scale"], out=ucat))
+                    emit(workload=w.name, kernel="lora_down_stacked", m=m, k=k,
+                         rank=int(a_cat.shape[0]), adapters=len(ads), us=round(tds * 1e3, 2),
+                         x_gbps=round(m * k * xb / (tds * 1e-3) / 1e9, 1))
+                    del a_cat
                 ys = [torch.empty((m, q.q.shape[0]), dtype=torch.float32, device="cuda") for q in lqws]
                 gl = w.gelu_chain
                 # Alternate the two launches and take medians: the first

@@ -199,6 +199,10 @@ convrot_status convrot_linear_grouped(const convrot_packed* x, const convrot_wei
  *   a : device bfloat16 [rank, k], row stride k
  *   u : device bfloat16 [m, ldu] (output; columns rank .. ldu-1 untouched, so
  *       several adapters' U can share one buffer)
+ * Adapters with the same scale on the same X (the Q, K and V projections of
+ * one block) can stack their A matrices, up to CONVROT_MAX_LORA_RANK rows in
+ * all, into one call that reads X once and writes each adapter's U as a
+ * column range of the shared buffer; each U column is computed the same way.
  *   rank a multiple of 16 in 16 .. CONVROT_MAX_LORA_RANK; k % 16 == 0;
  *   rank <= ldu <= 2^20 and ldu % 8 == 0;
  *   x, a, u 16-byte aligned, ldx in whole 16-byte units.
