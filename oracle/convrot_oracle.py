@@ -18,7 +18,7 @@ definition per step, with no blocking, fusion or reordering:
     4. A = Q_x Q_w^T in exact integers                [ICS, Runtime activation quantization]
     5. Y = A s_x[r] s_w[o] + b[o]                     [ICS, Runtime activation quantization]
 
-Readings where the page is silent (each is listed in the design doc as well):
+Readings where the page is silent:
 
 * ``round`` is round-half-away-from-zero (the C ``round`` function).
 * A row whose absmax is 0 gets scale 0 and all-zero codes.
@@ -293,7 +293,7 @@ def reference_linear_fp64(x, w, bias=None) -> np.ndarray:
 # low-rank form is used: with down weights A [r, K], up weights B [N, r] and a
 # scalar scale (alpha / r), the correction is  scale * (X A^T) B^T.
 #
-# Readings (listed in the design doc as well): the device computes in bfloat16
+# Readings: the device computes in bfloat16
 # operands with float32 accumulation, so the oracle takes the same operand
 # values -- X (bfloat16 as given, float32 inputs rounded to bfloat16), A and B
 # as bfloat16 values.  The rank-r intermediate carries the scale and is

@@ -1,6 +1,6 @@
 """GPU parity: the HIP path against the CPU oracle, through the C ABI.
 
-Tolerances (stated by the workload definition and derived in the design doc):
+Tolerances (stated by the workload definition):
   * Q_w and s_w bit-exact (both sides decide in float64);
   * Q_x within +-1 on at most 0.1% of elements, s_x within 1e-6 relative
     (the device rotates in float32 with a butterfly, the oracle rotates in

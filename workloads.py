@@ -5,7 +5,7 @@ method's arithmetic (no rotation, no scale, no quantisation).  The oracle and
 the HIP path both receive exactly the arrays made here, so their comparison
 starts from the same bits.
 
-Recipe (also stated in the design doc): ``numpy.random.default_rng(seed)``, draws in
+Recipe: ``numpy.random.default_rng(seed)``, draws in
 the fixed order X -> outlier columns or channel scales -> each W -> each b.
 
 * X ~ N(0, 1) float32, then either a set of outlier columns multiplied by a
