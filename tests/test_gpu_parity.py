@@ -8,9 +8,18 @@ Tolerances (stated by the workload definition):
   * A (raw int32) bit-exact when both sides get the same Q_x and Q_w;
   * Y within 1e-3 * s_x * s_w * K * 127 per element and a mean relative
     (aggregate L1) error of at most 1e-4 against the oracle's dequantised Y.
+The two code tolerances meet where K is small: one permitted change of a
+Q_x code moves Y by |Q_w[o, j]| s_x s_w, more than the per-element Y bound
+once |Q_w| > K / 1000 * 127 (K = 64: |Q_w| > 8).  Such a change can only
+happen where the float32 decision lies at a rounding tie, so the random-shape
+cases find those positions with the oracle (near_ties), require every
+changed code to sit at one, and add the exact effect of a change at each of
+them to the per-element Y bound (the mean relative bound is unchanged).
 Inputs come from workloads.py (seeded, shared by both sides); expected values
 come only from oracle/.
 """
+
+import os
 
 import numpy as np
 import pytest
@@ -27,6 +36,8 @@ S_REL = 1e-6
 Y_ELEM = 1e-3
 Y_MEAN_REL = 1e-4
 GELU_LIPSCHITZ = 1.13  # max |d/dx x*Phi(x)| = 1.1289...
+# seeded random-shape cases (a longer sweep: CONVROT_RANDOM_SEEDS=300)
+RANDOM_SEEDS = int(os.environ.get("CONVROT_RANDOM_SEEDS", "24"))
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -55,7 +66,32 @@ def host(t):
     return t.cpu().numpy()
 
 
-def check_pack(q_dev, s_dev, q_or, s_or, what=""):
+# Half-width, in code units, of the band around a rounding tie in which the
+# float32 decision v = x_rot / s_x may fall on either side: s_x's relative
+# tolerance at full scale (127 * 1e-6) plus the same again for the rotation's
+# float32 summation order.
+TIE_ETA = 127 * 2e-6
+
+
+def near_ties(x64, g):
+    """Positions whose oracle decision |x_rot / s_x| (float32 operands) lies
+    within TIE_ETA of a half-integer: the only codes that the rotation's
+    rounding order can move by one."""
+    xr = orc.rotate(x64, g).astype(np.float32).astype(np.float64)
+    _, sx = orc.pack_activations(x64, g)
+    s = sx.astype(np.float32).astype(np.float64)[:, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        a = np.where(s > 0, np.abs(xr) / np.where(s > 0, s, 1.0), 0.0)
+    return np.abs(a - np.floor(a) - 0.5) < TIE_ETA
+
+
+def flip_allowance(ties, qw_or, sx, sw):
+    """Per-element Y effect of a one-step change at every near-tie code."""
+    t = ties.astype(np.float64) @ np.abs(qw_or.astype(np.float64)).T
+    return t * sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :]
+
+
+def check_pack(q_dev, s_dev, q_or, s_or, what="", ties=None):
     q_dev = np.asarray(q_dev).astype(np.int32)
     q_or = np.asarray(q_or).astype(np.int32)
     assert q_dev.shape == q_or.shape
@@ -69,13 +105,18 @@ def check_pack(q_dev, s_dev, q_or, s_or, what=""):
     assert np.abs(d).max(initial=0) <= 1, f"{what}: code differs by {np.abs(d).max()}"
     frac = np.count_nonzero(d) / max(1, d.size)
     assert frac <= Q_MISMATCH_FRAC, f"{what}: {frac:.3%} codes differ"
+    if ties is not None:
+        off = np.count_nonzero((d != 0) & ~ties)
+        assert off == 0, f"{what}: {off} changed codes away from a rounding tie"
     assert q_dev.min(initial=0) >= -127 and q_dev.max(initial=0) <= 127
     return frac
 
 
-def check_y(y_dev, y_or, sx, sw, k, gelu=False, what=""):
+def check_y(y_dev, y_or, sx, sw, k, gelu=False, what="", allow=None):
     y_dev = np.asarray(y_dev, dtype=np.float64)
     bound = Y_ELEM * sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :] * k * 127
+    if allow is not None:
+        bound = bound + allow
     if gelu:
         bound = bound * GELU_LIPSCHITZ
     err = np.abs(y_dev - y_or)
@@ -578,7 +619,7 @@ def _random_case(rng, large):
             return m, k, g, ns
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(RANDOM_SEEDS))
 def test_random_shapes(seed):
     """Seeded random shapes through the pack and the grouped linear (raw
     int32, float32 or GELU output), against the oracle: ragged M, N and K,
@@ -601,7 +642,8 @@ def test_random_shapes(seed):
     _say(f"random shapes seed={seed}: m={m} k={k} G={g} n={ns} {xdt} {out}")
     p = cr.pack_activations(xt.cuda(), g)
     qx_or, sx_or = orc.pack_activations(x64, g)
-    check_pack(host(p.q), host(p.scale), qx_or, sx_or, f"seed {seed}")
+    ties = near_ties(x64, g)
+    check_pack(host(p.q), host(p.scale), qx_or, sx_or, f"seed {seed}", ties=ties)
     qws = [_prep(wt, b, g) for wt, b in zip(wts, bs)]
     ors = [orc.quantize_weights(wt, g) for wt in wts]
     for qw, (qw_or, sw_or) in zip(qws, ors):
@@ -616,7 +658,8 @@ def test_random_shapes(seed):
         ys = cr.linear_grouped(p, qws, gelu=gelu)
         for i, (y, (qw_or, sw_or), b) in enumerate(zip(ys, ors, bs)):
             y_or = orc.linear(qx_or, sx_or, qw_or, sw_or, b, act="gelu" if gelu else None)
-            check_y(host(y), y_or, sx_or, sw_or, k, gelu=gelu, what=f"seed {seed} w{i}")
+            check_y(host(y), y_or, sx_or, sw_or, k, gelu=gelu, what=f"seed {seed} w{i}",
+                    allow=flip_allowance(ties, qw_or, sx_or, sw_or))
 
 
 def test_helpers_reject_bad_tensors():
@@ -873,10 +916,13 @@ def _fused_case(m, n_list, rank_list, k=3072, seed=21, gelu=False, g=256):
         ads.append(ad)
     ys = cr.linear_lora(p, ws, adapters, gelu=gelu)
     qx_or, sx_or = orc.pack_activations(inp["x64"], g)
+    ties = near_ties(inp["x64"], g)
+    check_pack(host(p.q), host(p.scale), qx_or, sx_or, f"fused m={m}", ties=ties)
     for i, (y, wt, b, ad) in enumerate(zip(ys, inp["weights"], inp["biases"], ads)):
         qw_or, sw_or = orc.quantize_weights(wt, g)
         pre = orc.linear(qx_or, sx_or, qw_or, sw_or, b)
         bound = Y_ELEM * sx_or.astype(np.float64)[:, None] * sw_or.astype(np.float64)[None, :] * k * 127
+        bound = bound + flip_allowance(ties, qw_or, sx_or, sw_or)
         if ad is not None:
             u_or, eps_u, lb, corr = _lora_bounds(inp["x64"], ad)
             pre = pre + corr
@@ -902,7 +948,7 @@ def test_linear_lora_fused(m, ns, ranks):
     _fused_case(m, ns, ranks)
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(max(1, RANDOM_SEEDS // 3)))
 def test_linear_lora_fused_random(seed):
     """Seeded random shapes and ranks (0 = no adapter) for the fused path."""
     rng = np.random.default_rng(2000 + seed)
