@@ -12,9 +12,12 @@ The two code tolerances meet where K is small: one permitted change of a
 Q_x code moves Y by |Q_w[o, j]| s_x s_w, more than the per-element Y bound
 once |Q_w| > K / 1000 * 127 (K = 64: |Q_w| > 8).  Such a change can only
 happen where the float32 decision lies at a rounding tie, so the random-shape
-cases find those positions with the oracle (near_ties), require every
-changed code to sit at one, and add the exact effect of a change at each of
-them to the per-element Y bound (the mean relative bound is unchanged).
+and fused-adapter cases find those positions with the oracle (near_ties),
+require every changed code to sit at one (a one-step change, at most 0.1 %
+of codes, as before), and add the exact effect of the changes to the Y
+bounds: sum |Q_w[o, j]| s_x s_w over the changed positions j of row r to
+the per-element bound, and its total to the aggregate one.  The expected Y
+is still the oracle's alone.
 Inputs come from workloads.py (seeded, shared by both sides); expected values
 come only from oracle/.
 """
@@ -36,7 +39,7 @@ S_REL = 1e-6
 Y_ELEM = 1e-3
 Y_MEAN_REL = 1e-4
 GELU_LIPSCHITZ = 1.13  # max |d/dx x*Phi(x)| = 1.1289...
-# seeded random-shape cases (a longer sweep: CONVROT_RANDOM_SEEDS=300)
+# seeded random-shape cases (a longer sweep: CONVROT_RANDOM_SEEDS=1000)
 RANDOM_SEEDS = int(os.environ.get("CONVROT_RANDOM_SEEDS", "24"))
 
 
@@ -85,9 +88,9 @@ def near_ties(x64, g):
     return np.abs(a - np.floor(a) - 0.5) < TIE_ETA
 
 
-def flip_allowance(ties, qw_or, sx, sw):
-    """Per-element Y effect of a one-step change at every near-tie code."""
-    t = ties.astype(np.float64) @ np.abs(qw_or.astype(np.float64)).T
+def flip_allowance(changed, qw_or, sx, sw):
+    """Per-element Y effect of a one-step change at every flagged code."""
+    t = changed.astype(np.float64) @ np.abs(qw_or.astype(np.float64)).T
     return t * sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :]
 
 
@@ -115,15 +118,18 @@ def check_pack(q_dev, s_dev, q_or, s_or, what="", ties=None):
 def check_y(y_dev, y_or, sx, sw, k, gelu=False, what="", allow=None):
     y_dev = np.asarray(y_dev, dtype=np.float64)
     bound = Y_ELEM * sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :] * k * 127
+    extra = 0.0
     if allow is not None:
         bound = bound + allow
+        extra = allow.sum() * (GELU_LIPSCHITZ if gelu else 1.0)
     if gelu:
         bound = bound * GELU_LIPSCHITZ
     err = np.abs(y_dev - y_or)
     worst = np.max(err - bound)
     assert worst <= 0, f"{what}: per-element bound exceeded by {worst:.3g}"
     rel = err.sum() / np.abs(y_or).sum()
-    assert rel <= Y_MEAN_REL, f"{what}: mean relative error {rel:.3g}"
+    assert err.sum() <= Y_MEAN_REL * np.abs(y_or).sum() + extra, \
+        f"{what}: mean relative error {rel:.3g}"
     return rel
 
 
@@ -644,6 +650,7 @@ def test_random_shapes(seed):
     qx_or, sx_or = orc.pack_activations(x64, g)
     ties = near_ties(x64, g)
     check_pack(host(p.q), host(p.scale), qx_or, sx_or, f"seed {seed}", ties=ties)
+    changed = host(p.q).astype(np.int32) != qx_or.astype(np.int32)  # all at ties
     qws = [_prep(wt, b, g) for wt, b in zip(wts, bs)]
     ors = [orc.quantize_weights(wt, g) for wt in wts]
     for qw, (qw_or, sw_or) in zip(qws, ors):
@@ -659,7 +666,7 @@ def test_random_shapes(seed):
         for i, (y, (qw_or, sw_or), b) in enumerate(zip(ys, ors, bs)):
             y_or = orc.linear(qx_or, sx_or, qw_or, sw_or, b, act="gelu" if gelu else None)
             check_y(host(y), y_or, sx_or, sw_or, k, gelu=gelu, what=f"seed {seed} w{i}",
-                    allow=flip_allowance(ties, qw_or, sx_or, sw_or))
+                    allow=flip_allowance(changed, qw_or, sx_or, sw_or))
 
 
 def test_helpers_reject_bad_tensors():
@@ -918,11 +925,13 @@ def _fused_case(m, n_list, rank_list, k=3072, seed=21, gelu=False, g=256):
     qx_or, sx_or = orc.pack_activations(inp["x64"], g)
     ties = near_ties(inp["x64"], g)
     check_pack(host(p.q), host(p.scale), qx_or, sx_or, f"fused m={m}", ties=ties)
+    changed = host(p.q).astype(np.int32) != qx_or.astype(np.int32)  # all at ties
     for i, (y, wt, b, ad) in enumerate(zip(ys, inp["weights"], inp["biases"], ads)):
         qw_or, sw_or = orc.quantize_weights(wt, g)
         pre = orc.linear(qx_or, sx_or, qw_or, sw_or, b)
         bound = Y_ELEM * sx_or.astype(np.float64)[:, None] * sw_or.astype(np.float64)[None, :] * k * 127
-        bound = bound + flip_allowance(ties, qw_or, sx_or, sw_or)
+        allow = flip_allowance(changed, qw_or, sx_or, sw_or)
+        bound = bound + allow
         if ad is not None:
             u_or, eps_u, lb, corr = _lora_bounds(inp["x64"], ad)
             pre = pre + corr
@@ -933,7 +942,8 @@ def _fused_case(m, n_list, rank_list, k=3072, seed=21, gelu=False, g=256):
         err = np.abs(host(y).astype(np.float64) - y_or)
         what = f"fused m={m} w{i} n={wt.shape[0]} r={rank_list[i]}{' gelu' if gelu else ''}"
         assert np.all(err <= bound), f"{what}: bound exceeded by {np.max(err - bound):.3g}"
-        assert err.sum() / np.abs(y_or).sum() <= Y_MEAN_REL, what
+        extra = allow.sum() * (GELU_LIPSCHITZ if gelu else 1.0)
+        assert err.sum() <= Y_MEAN_REL * np.abs(y_or).sum() + extra, what
     return ys
 
 
