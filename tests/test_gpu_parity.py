@@ -241,6 +241,42 @@ def test_pack_rows_split_over_waves(k, g, dt, m):
     check_pack(host(p.q), host(p.scale), q_or, s_or, f"k={k} G={g} m={m}")
 
 
+@pytest.mark.parametrize("seed", range(RANDOM_SEEDS))
+def test_random_pack(seed):
+    """Seeded random activations through the pack kernels: K a multiple of 16
+    up to 32768 (rows split over waves included), every power-of-four G
+    dividing K, bf16 or float32, a padded row stride on odd seeds, outlier
+    columns, per-channel spread, zero and constant rows; codes and scales
+    against the oracle, every changed code a one-step change at a tie."""
+    rng = np.random.default_rng(5000 + seed)
+    while True:
+        k = 16 * int(rng.integers(1, 2049))
+        m = int(rng.integers(1, 400))
+        if m * k <= 4_000_000:
+            break
+    g = int(rng.choice([4 ** n for n in range(8) if k % 4 ** n == 0]))
+    dt = "bf16" if seed % 3 else "f32"
+    pad = 8 * int(rng.integers(1, 5)) if seed % 2 else 0
+    x32 = rng.standard_normal((m, k + pad)).astype(np.float32)
+    x32[:, rng.choice(k, max(1, k // 500), replace=False)] *= float(rng.uniform(1, 50))
+    if seed % 4 == 1:
+        x32 *= rng.lognormal(0.0, 1.0, k + pad).astype(np.float32)[None, :]
+    if m > 3:
+        x32[int(rng.integers(0, m))] = 0
+        x32[int(rng.integers(0, m))] = np.float32(rng.uniform(-3, 3))
+    if dt == "bf16":
+        full = torch.from_numpy(x32).to(torch.bfloat16)
+        x64 = full.to(torch.float64).numpy()[:, :k]
+    else:
+        full = torch.from_numpy(x32)
+        x64 = x32[:, :k].astype(np.float64)
+    xt = full.cuda()[:, :k]
+    _say(f"random pack seed={seed}: m={m} k={k} G={g} {dt} pad={pad}")
+    p = cr.pack_activations(xt, g)
+    q_or, s_or = orc.pack_activations(x64, g)
+    check_pack(host(p.q), host(p.scale), q_or, s_or, f"seed {seed}", ties=near_ties(x64, g))
+
+
 def test_pack_strided_input_and_reuse_of_output():
     rng = np.random.default_rng(8)
     big = rng.standard_normal((40, 2048 + 64)).astype(np.float32)
