@@ -99,6 +99,10 @@ def _module(name: str, tensors: dict) -> ConvrotModule:
     if w.dtype != torch.int8 or w.dim() != 2:
         raise CheckpointError(f"{name}.weight must be a 2-D int8 tensor, got {w.dtype} {tuple(w.shape)}")
     n, k = w.shape
+    if w.numel() and int(w.min()) < -127:
+        # The page's section "Weight quantization" clamps codes to [-127, 127];
+        # -128 would also break the int32 range the GEMM's K limit is sized for.
+        raise CheckpointError(f"{name}.weight holds the code -128, outside [-127, 127]")
     if s.dtype not in _FLOAT_DTYPES:
         raise CheckpointError(f"{name}.weight_scale must be floating point, got {s.dtype}")
     if tuple(s.shape) == (n, 1):

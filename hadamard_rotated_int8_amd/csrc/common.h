@@ -74,21 +74,30 @@ CR_DEVICE float dpp_f32(float v) {
 CR_DEVICE float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 CR_DEVICE float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
 
-// Round half away from zero, then to int32, for |v| <= 128.
-// trunc(v + copysign(0.5 - 2^-25, v)) equals round-half-away for every float32
-// of magnitude at most 128 (checked exhaustively on the host); the float->int
-// conversion truncates toward zero.
-CR_DEVICE int round_half_away_small(float v) {
-  return (int)(v + __builtin_copysignf(0.49999997f, v));
+// Activation code of a rotated value x, given r = RN(1/s) for the row scale s:
+// round half away from zero of x r, as trunc(RN(x r + copysign(0.5 - 2^-25, x)))
+// -- one fused multiply-add; the float->int conversion truncates toward zero.
+// With r = 1 this is exactly round-half-away of x for every float32 |x| <= 128
+// (checked exhaustively on the host).  For other scales x r differs from the
+// correctly rounded x / s by at most about one unit in the last place, so a
+// code can differ from round(x / s) only where x / s lies within a few ulp of a
+// half-integer.  r = 0 (a zero row) gives 0.
+CR_DEVICE int code_of(float x, float r) {
+  return (int)__builtin_fmaf(x, r, __builtin_copysignf(0.49999997f, x));
 }
 
-// Correctly rounded float32 quotient x / b from r = RN(1/b): one product, one
-// residual and one correction (Markstein's theorem for round-to-nearest).
-CR_DEVICE float div_by_recip(float x, float b, float r) {
-  float q = x * r;
-  float e = __builtin_fmaf(-q, b, x);
-  return __builtin_fmaf(e, r, q);
+// The same, clamped to [-127, 127]: for rows whose scale is subnormal, where
+// the scale's own rounding can put |x r| above 127.5.
+CR_DEVICE int code_of_clamped(float x, float r) {
+  const float f = __builtin_fmaf(x, r, __builtin_copysignf(0.49999997f, x));
+  return (int)__builtin_amdgcn_fmed3f(f, -127.0f, 127.0f);
 }
+
+// Rows whose absmax is below kTinyRowMax take the pre-scaled path: x and the
+// scale are both multiplied by 2^64 (exact), so 1/s cannot overflow float32
+// (it would for s below 2^-128), and the codes are clamped.
+constexpr float kTinyRowMax = 0x1p-100f;
+constexpr float kTinyRowScale = 0x1p64f;
 
 CR_DEVICE int clamp127(int q) { return max(-127, min(127, q)); }
 

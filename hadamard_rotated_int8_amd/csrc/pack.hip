@@ -22,9 +22,13 @@
 //     factor 2^n is exact and is taken out of the scale, so every rounding is
 //     that of the normalised butterfly;
 //   * the row absmax is reduced across lanes and then across waves in LDS;
-//   * the code decision is made in float32: s = m/127 (IEEE division), then
-//     v = RN(x/s) via a correctly rounded reciprocal plus one FMA correction,
-//     then round-half-away; the int8 codes leave as 16-byte stores.
+//   * the code decision is made in float32: s = m/127 (IEEE division) and
+//     r = RN(1/s) once per row, then per value one fused multiply-add,
+//     trunc(RN(x r + copysign(0.5 - 2^-25, x))): round half away from zero of
+//     x r (exact for s = 1; otherwise equal to round(x / s) except within a
+//     few ulp of a half-integer); rows with a tiny absmax are pre-scaled by
+//     2^64 so that 1/s cannot overflow; the int8 codes leave as 16-byte
+//     stores.
 //
 // Fast path (pack_rows_kernel), used when G <= 1024 and K is a multiple of
 // 1024 (every row then splits into whole 64-chunk wave loads): one wave owns
@@ -212,6 +216,23 @@ CR_DEVICE void load_rotate_segment(const InT* __restrict__ xr, int seg, int nch,
   }
 }
 
+// Scale of a row from the absmax mx of its unnormalised rotation (2^n X_rot):
+// s = (mx 2^-n) / 127, the value stored.  Returns s; sets r = RN(1 / s_un),
+// the reciprocal the codes use (s_un = s 2^n, so x_un / s_un == x / s
+// exactly), with r = 0 for a zero row.  Rows whose absmax is below
+// kTinyRowMax are "tiny": r is formed for s_un 2^64 instead, and their
+// values must be multiplied by 2^64 (exactly) and their codes clamped.
+CR_DEVICE float row_scale(float mx, int log4g, float& r, bool& tiny) {
+  mx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mx)));  // uniform: one per row
+  const float m = ldexpf(mx, -log4g);
+  const float s = m / 127.0f;
+  tiny = m < kTinyRowMax;
+  float s_un = ldexpf(s, log4g);
+  if (tiny) s_un *= kTinyRowScale;
+  r = (s_un != 0.f) ? 1.0f / s_un : 0.f;
+  return s;
+}
+
 template <int CPT>
 CR_DEVICE float local_absmax(const float (&v)[CPT][16]) {
   float m = 0.f;
@@ -223,7 +244,7 @@ CR_DEVICE float local_absmax(const float (&v)[CPT][16]) {
 }
 
 template <int CPT>
-CR_DEVICE void quantize_store(const float (&v)[CPT][16], int seg, int nch, float s_un, float r,
+CR_DEVICE void quantize_store(float (&v)[CPT][16], int seg, int nch, float r, bool tiny,
                               int8_t* __restrict__ qr, int t, int T) {
   const int tp = chunk_of_thread(t);
 #pragma unroll
@@ -231,13 +252,12 @@ CR_DEVICE void quantize_store(const float (&v)[CPT][16], int seg, int nch, float
     const int j = (seg * CPT + c) * T + tp;
     if (j >= nch) continue;
     int qi[16];
-    if (s_un != 0.f) {
+    if (!tiny) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        qi[e] = clamp127(round_half_away_small(div_by_recip(v[c][e], s_un, r)));
+      for (int e = 0; e < 16; ++e) qi[e] = code_of(v[c][e], r);
     } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) qi[e] = 0;
+      for (int e = 0; e < 16; ++e) qi[e] = code_of_clamped(v[c][e] * kTinyRowScale, r);
     }
     uint4 o;
     o.x = pack4(qi[0], qi[1], qi[2], qi[3]);
@@ -279,17 +299,16 @@ __global__ __launch_bounds__(1024) void pack_kernel(const InT* __restrict__ x, i
     for (int w = 1; w < nwaves; ++w) mx = fmaxf(mx, wave_max[w]);
     __syncthreads();  // wave_max is rewritten for the next row
 
-    // Undo the unnormalised butterfly's exact factor 2^n, then s = max / 127.
-    const float s = ldexpf(mx, -log4g) / 127.0f;
+    bool tiny;
+    float r;
+    const float s = row_scale(mx, log4g, r, tiny);
     if (t == 0) scale[row] = s;
-    const float s_un = ldexpf(s, log4g);  // x_un / s_un == x / s exactly
-    const float r = (s_un != 0.f) ? 1.0f / s_un : 0.f;
     if (nseg == 1) {
-      quantize_store<CPT>(v, 0, nch, s_un, r, qr, t, T);
+      quantize_store<CPT>(v, 0, nch, r, tiny, qr, t, T);
     } else {
       for (int seg = 0; seg < nseg; ++seg) {
         load_rotate_segment<InT, CPT>(xr, seg, nch, log4g, v, lds_buf, t, T);
-        quantize_store<CPT>(v, seg, nch, s_un, r, qr, t, T);
+        quantize_store<CPT>(v, seg, nch, r, tiny, qr, t, T);
       }
     }
   }
@@ -476,20 +495,21 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const InT* __restrict__ 
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(v[c][e]));
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    // Undo the unnormalised butterfly's exact factor 2^n, then s = max / 127.
-    const float s = ldexpf(mx, -log4g) / 127.0f;
+    bool tiny;
+    float r;
+    const float s = row_scale(mx, log4g, r, tiny);
     if (lane == 0) scale[row] = s;
-    const float s_un = ldexpf(s, log4g);  // x_un / s_un == x / s exactly
-    // A zero row (s_un == 0) has only zeros, and with r = 0 the quotient
-    // below is then 0 as well: no per-element test is needed.
-    const float r = (s_un != 0.f) ? 1.0f / s_un : 0.f;
     int8_t* qr = q + (int64_t)row * k;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       int qi[16];
+      if (!tiny) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        qi[e] = clamp127(round_half_away_small(div_by_recip(v[c][e], s_un, r)));
+        for (int e = 0; e < 16; ++e) qi[e] = code_of(v[c][e], r);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) qi[e] = code_of_clamped(v[c][e] * kTinyRowScale, r);
+      }
       uint4 o;
       o.x = pack4_perm(qi[0], qi[1], qi[2], qi[3]);
       o.y = pack4_perm(qi[4], qi[5], qi[6], qi[7]);
@@ -505,8 +525,10 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const InT* __restrict__ 
 // butterfly stage is a register stage (two adds per element) and the lane
 // exchange is LDS traffic instead of VALU work.  The codes return to the
 // natural layout by a byte transpose through the same LDS buffer and leave
-// as 16-byte stores.  A row's maximum satisfies |x| <= max, so
-// |x / s| <= 127 (1 + 2^-23) and the code needs no clamp.
+// as 16-byte stores.  For a row whose absmax m is not tiny, every |x| <= m
+// and r = RN(1 / RN(m / 127)), so |x r| <= 127 (1 + 2^-23) and
+// trunc(RN(|x r| + 0.5 - 2^-25)) <= 127: the code needs no clamp (tiny rows,
+// whose subnormal scale may be rounded by far more, take the clamped path).
 // The 16 x 16 float transpose of a 16-lane group: lane li writes its 16
 // values as row li (four 16-byte writes) and reads column li back.  Rows are
 // kTRow = 20 floats apart, so the 16 row starts of a write fall on 16
@@ -602,10 +624,10 @@ __global__ __launch_bounds__(256) void pack_rows_lds_kernel(const InT* __restric
       for (int w2 = 0; w2 < WPR; ++w2) mx = fmaxf(mx, red[it & 1][(wv / WPR) * WPR + w2]);
     }
     if (!live) continue;
-    const float s = ldexpf(mx, -log4g) / 127.0f;
+    bool tiny;
+    float r;
+    const float s = row_scale(mx, log4g, r, tiny);
     if (lane == 0 && part == 0) scale[row] = s;
-    const float s_un = ldexpf(s, log4g);
-    const float r = (s_un != 0.f) ? 1.0f / s_un : 0.f;  // zero rows: codes 0 (see above)
     // The codes go back to the natural layout through LDS as bytes (lane li
     // writes byte li of each of its 16 chunks; lane li then reads chunk li
     // whole), so each chunk leaves as one 16-byte store.  The float
@@ -615,9 +637,14 @@ __global__ __launch_bounds__(256) void pack_rows_lds_kernel(const InT* __restric
     int8_t* qr = q + (int64_t)row * k + col0 + (16 * grp + li) * 16;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
+      if (!tiny) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        tb[i * 16 + li] = (int8_t)round_half_away_small(div_by_recip(t[c][i], s_un, r));
+        for (int i = 0; i < 16; ++i) tb[i * 16 + li] = (int8_t)code_of(t[c][i], r);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          tb[i * 16 + li] = (int8_t)code_of_clamped(t[c][i] * kTinyRowScale, r);
+      }
       *reinterpret_cast<u32x4*>(qr + c * 64 * 16) = *reinterpret_cast<const u32x4*>(tb + li * 16);
     }
   }

@@ -85,7 +85,7 @@ def _cfg(**kw):
 
 @pytest.mark.parametrize("case", ["missing_scale", "float_weight", "bad_json", "format", "no_convrot",
                                   "group_not_pow4", "group_bool", "group_not_dividing",
-                                  "scale_shape", "negative_scale", "bias_shape"])
+                                  "scale_shape", "negative_scale", "bias_shape", "code_minus_128"])
 def test_rejections(tmp_path, case):
     q = torch.zeros((4, 32), dtype=torch.int8)
     t = {"m.weight": q, "m.weight_scale": torch.ones(4), "m.comfy_quant": _cfg()}
@@ -111,6 +111,10 @@ def test_rejections(tmp_path, case):
         t["m.weight_scale"] = -torch.ones(4)
     elif case == "bias_shape":
         t["m.bias"] = torch.ones(3)
+    elif case == "code_minus_128":
+        q = q.clone()
+        q[2, 7] = -128
+        t["m.weight"] = q
     with pytest.raises(ck.CheckpointError):
         ck.load_checkpoint(_write(tmp_path, t))
 
