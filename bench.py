@@ -307,6 +307,64 @@ def cpu_baseline(inp, w, g, target_s):
     }
 
 
+def _ceiling_lib():
+    """The measurement library (include/convrot_ceiling.h), or None if absent."""
+    import ctypes
+
+    path = os.path.join(ROOT, "hadamard_rotated_int8_amd", "libconvrot_ceiling.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    f = lib.convrot_ceiling_mfma_i8
+    f.restype = ctypes.c_int64
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+def mfma_ceiling(qa, qb, reps=5):
+    """Rate of a register-only v_mfma_i32_32x32x32_i8 loop in the GEMM's
+    per-wave shape, one wave per SIMD on every CU, on fragments of the given
+    int8 codes (TOPS, median of reps launches of ~2 ms).  None without the
+    measurement library."""
+    import torch
+
+    lib = _ceiling_lib()
+    if lib is None:
+        return None
+    grid = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    iters = 4000
+    ts, ops = [], 0
+    for _ in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ops = lib.convrot_ceiling_mfma_i8(qa.data_ptr(), qa.stride(0), qa.shape[0], qb.data_ptr(),
+                                          qb.stride(0), qb.shape[0], iters, grid, sink.data_ptr(),
+                                          stream)
+        e1.record()
+        torch.cuda.synchronize()
+        if ops < 0:
+            raise RuntimeError("MFMA ceiling kernel refused its arguments")
+        ts.append(e0.elapsed_time(e1))
+    return ops / (float(np.median(ts[1:])) * 1e-3) / 1e12
+
+
+def copy_ceiling(nbytes, flush, reps=20):
+    """GB/s of a plain device copy that reads and writes nbytes / 2 each (the
+    pack's algorithmic byte count), warm and after a cache-flushing write."""
+    import torch
+
+    half = nbytes // 2 // 4
+    src = torch.ones(half, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    warm = _time_ms(lambda: dst.copy_(src), reps=reps)
+    cold = _time_ms(lambda: dst.copy_(src), reps=reps, flush=flush)
+    moved = 2 * half * 4
+    return moved / (warm * 1e-3) / 1e9, moved / (cold * 1e-3) / 1e9
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -341,6 +399,21 @@ def main():
                                  torch.empty((m,), dtype=torch.float32, device="cuda"), g)
     ys = [torch.empty((m, q.q.shape[0]), dtype=torch.float32, device="cuda") for q in qws]
     torch.cuda.synchronize()
+    pack_bytes = m * k * (2 if x.dtype == torch.bfloat16 else 4) + m * k + 4 * m
+
+    # Before the step loop: the pack alone (warm: back-to-back launches; cold:
+    # after a 512 MB cache-flushing write), a plain copy of the same byte
+    # count, and the matrix cores' rate on these operand codes.  Besides their
+    # own figures these runs bring the shader clock to the steady state it
+    # holds under sustained work before the warm-up steps begin.
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    pack_avg_ms = _time_ms(lambda: cr.pack_activations(x, g, out=packed), reps=50)
+    pack_cold_ms = _time_ms(lambda: cr.pack_activations(x, g, out=packed), reps=20, flush=flush)
+    copy_warm_gbps, copy_cold_gbps = copy_ceiling(pack_bytes, flush)
+    del flush
+    mfma_loop_tops = mfma_ceiling(packed.q, qws[0].q)
+    pack_gbps = pack_bytes / (pack_avg_ms * 1e-3) / 1e9
+    pack_cold_gbps = pack_bytes / (pack_cold_ms * 1e-3) / 1e9
 
     # Events are recorded on the current stream, the one the library launches
     # on.  A timed event costs about 2 us of stream time here, so the GEMM's
@@ -383,32 +456,7 @@ def main():
     gemm_ops_per_launch = ops  # one grouped launch covers all three weights
     gemm_avg_ms = float(gemm_ms.mean())
     gemm_tops = gemm_ops_per_launch / (gemm_avg_ms * 1e-3) / 1e12
-    pack_bytes = m * k * (2 if x.dtype == torch.bfloat16 else 4) + m * k + 4 * m
-
-    # The pack alone, warm: back-to-back launches after the timed region.
-    pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    pe0.record()
-    for _ in range(50):
-        cr.pack_activations(x, g, out=packed)
-    pe1.record()
-    torch.cuda.synchronize()
-    pack_avg_ms = pe0.elapsed_time(pe1) / 50
-    pack_gbps = pack_bytes / (pack_avg_ms * 1e-3) / 1e9
-
-    # Pack with the caches flushed (a 512 MB write between launches; not in the step).
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
-    cold = []
-    for _ in range(20):
-        flush.fill_(1.0)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        cr.pack_activations(x, g, out=packed)
-        e1.record()
-        torch.cuda.synchronize()
-        cold.append(e0.elapsed_time(e1))
-    del flush
-    pack_cold_ms = float(np.median(cold))
+    traffic = gemm_traffic()
 
     out = {
         "metric": "convrot linear effective INT8 TOPS at 4096x3072x9216; act-pack HBM GB/s",
@@ -435,17 +483,27 @@ def main():
         "pack_us_warm": round(pack_avg_ms * 1e3, 3),
         "pack_gbps_warm": round(pack_gbps, 1),
         "pack_us_cold": round(pack_cold_ms * 1e3, 3),
-        "pack_gbps_cold": round(pack_bytes / (pack_cold_ms * 1e-3) / 1e9, 1),
-        "pack_hbm_frac_cold": round(pack_bytes / (pack_cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "pack_gbps_cold": round(pack_cold_gbps, 1),
+        "pack_hbm_frac_cold": round(pack_cold_gbps / PEAK_HBM_GBPS, 4),
+        "copy_gbps_warm": round(copy_warm_gbps, 1),
+        "copy_gbps_cold": round(copy_cold_gbps, 1),
+        "pack_frac_of_copy_cold": round(pack_cold_gbps / copy_cold_gbps, 4),
+        "mfma_loop_tops": None if mfma_loop_tops is None else round(mfma_loop_tops, 1),
+        "gemm_frac_of_mfma_loop": (None if mfma_loop_tops is None
+                                   else round(gemm_tops / mfma_loop_tops, 4)),
         "wall_s_timed": round(wall, 3),
         "roofline": {
             "bound": "mfma",
-            "kernel": "gemm_i8_kernel<192,0> (grouped Q, K, V: 4096 x 9216 x 3072)",
+            "kernel": "gemm_i8_kernel (grouped Q, K, V: 4096 x 9216 x 3072)",
             "achieved": round(gemm_tops, 2),
             "peak": PEAK_INT8_TOPS,
+            # tera-operations per second (int8 multiply-add = 2 operations)
             "unit": "TFLOP/s",
             "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
-            "traffic": gemm_traffic(),
+            "traffic": traffic,
+            "traffic_source": (None if traffic is None else
+                               "profiles/gemm_qkv_4096x3072x9216_traffic.json: rocprofv3 FETCH_SIZE + "
+                               "WRITE_SIZE per launch, scaled by a plain copy, taken on this gemm.hip"),
         },
     }
     if not args.no_cpu_baseline:

@@ -3,7 +3,9 @@
 Usage: python -m hadamard_rotated_int8_amd.build  (or build() from Python)
 
 Every call recompiles all sources: objects go to _build/ at the repository
-root, the shared library next to this file.
+root, the shared libraries next to this file.  Besides the layer's library,
+libconvrot_ceiling.so holds the measurement kernel the benchmark times
+beside the GEMM (include/convrot_ceiling.h); nothing on the hot path uses it.
 """
 
 from __future__ import annotations
@@ -20,9 +22,11 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libconvrot.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+CEILING_LIB_PATH = os.path.join(PKG_DIR, "libconvrot_ceiling.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "pack.hip", "wprep.hip", "gemm.hip", "gemm_small.hip", "lora.hip"]
+CEILING_SOURCES = ["ceiling.hip"]
 
 # Packed-FP32 instructions are kept out of generated code on purpose.
 COMMON_FLAGS = [
@@ -59,20 +63,27 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(extra_flags: list[str] | None = None, verbose: bool = False) -> str:
-    """Compile every source and link libconvrot.so; returns its path."""
-    extra = list(extra_flags or [])
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs: list[str], path: str) -> None:
+    tmp = path + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(extra_flags: list[str] | None = None, verbose: bool = False) -> str:
+    """Compile every source, link libconvrot.so and libconvrot_ceiling.so;
+    returns the path of libconvrot.so."""
+    extra = list(extra_flags or [])
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    sources = SOURCES + CEILING_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(sources), 8)) as ex:
+        objs = dict(zip(sources, ex.map(lambda s: _compile(s, extra), sources)))
+    _link([objs[s] for s in SOURCES], LIB_PATH)
+    _link([objs[s] for s in CEILING_SOURCES], CEILING_LIB_PATH)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {CEILING_LIB_PATH}")
     return LIB_PATH
 
 

@@ -40,6 +40,25 @@ def test_library_exports_every_declared_function():
         assert hasattr(L, name), name
 
 
+def test_ceiling_library_exports_its_declared_function():
+    """libconvrot_ceiling.so (the benchmark's measurement kernel) exports what
+    include/convrot_ceiling.h declares, and refuses bad arguments on the host."""
+    text = open(os.path.join(ROOT, "include", "convrot_ceiling.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(convrot_\w+)\s*\(", text)))
+    assert names == ["convrot_ceiling_mfma_i8"]
+    L = ctypes.CDLL(os.path.join(ROOT, "hadamard_rotated_int8_amd", "libconvrot_ceiling.so"))
+    f = L.convrot_ceiling_mfma_i8
+    f.restype = ctypes.c_int64
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(None, 128, 32, FAKE, 128, 32, 1, 1, FAKE, None) == -1      # null operand
+    assert f(FAKE, 120, 32, FAKE, 128, 32, 1, 1, FAKE, None) == -1      # row stride < 128
+    assert f(FAKE, 128, 31, FAKE, 128, 32, 1, 1, FAKE, None) == -1      # fewer than 32 rows
+    assert f(FAKE, 128, 32, FAKE, 128, 32, 0, 1, FAKE, None) == -1      # no iterations
+    assert f(FAKE + 8, 128, 32, FAKE, 128, 32, 1, 1, FAKE, None) == -1  # misaligned
+
+
 def test_header_constants_match_binding():
     text = open(HEADER).read()
     assert int(re.search(r"#define CONVROT_MAX_K (\d+)", text).group(1)) == cr.MAX_K
