@@ -102,6 +102,22 @@ def _time_ms(fn, reps=20, flush=None):
     return float(np.median(ts))
 
 
+def copy_beside(nbytes, pack_warm_ms, pack_cold_ms, flush):
+    """A plain device copy moving the pack's byte count (reads and writes
+    nbytes / 2 each), warm and cold, and the pack's time as a fraction of it."""
+    import torch
+
+    half = nbytes // 2 // 4
+    src = torch.ones(half, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    warm = _time_ms(lambda: dst.copy_(src))
+    cold = _time_ms(lambda: dst.copy_(src), reps=10, flush=flush)
+    del src, dst
+    return {"copy_us_warm": round(warm * 1e3, 2), "copy_us_cold": round(cold * 1e3, 2),
+            "copy_over_pack_warm": round(warm / pack_warm_ms, 4),
+            "copy_over_pack_cold": round(cold / pack_cold_ms, 4)}
+
+
 def all_configs(args):
     """Every workload: the pack per group size and each linear, as JSON lines."""
     import torch
@@ -143,7 +159,8 @@ def all_configs(args):
             emit(workload=w.name, kernel="pack", m=m, k=k, x_dtype=w.x_dtype, group_size=g,
                  us_warm=round(warm * 1e3, 2), us_cold=round(cold * 1e3, 2),
                  gbps_cold=round(pbytes / (cold * 1e-3) / 1e9, 1),
-                 hbm_frac_cold=round(pbytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4))
+                 hbm_frac_cold=round(pbytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                 **copy_beside(pbytes, warm, cold, flush))
             linears = list(zip(w.linears, qws))
             if w.gelu_chain:
                 linears = linears[:1]
@@ -164,7 +181,8 @@ def all_configs(args):
                     emit(workload=w.name, kernel="pack", m=m, k=spec.n, x_dtype="f32", group_size=g,
                          us_warm=round(hwarm * 1e3, 2), us_cold=round(hcold * 1e3, 2),
                          gbps_cold=round(hbytes / (hcold * 1e-3) / 1e9, 1),
-                         hbm_frac_cold=round(hbytes / (hcold * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4))
+                         hbm_frac_cold=round(hbytes / (hcold * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                         **copy_beside(hbytes, hwarm, hcold, flush))
                     yd = torch.empty((m, dspec.n), dtype=torch.float32, device="cuda")
                     td = _time_ms(lambda: cr.linear(hp, dqw, out=yd))
                     dtops = 2.0 * m * dspec.n * spec.n / (td * 1e-3) / 1e12

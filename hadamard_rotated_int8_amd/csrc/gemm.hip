@@ -420,7 +420,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
 
   // ------------------------------------------------------------ prologue
   // Q_x of step 0, Q_w of steps 0 and 1; after the barrier the first Q_x
-  // pieces of step 1.
+  // pieces of step 1.  Only step 0's operands are waited for here: Q_w of
+  // step 1 (the last WPW loads) lands under step 0, whose closing wait
+  // covers it.
   begin_x();
 #pragma unroll
   for (int i = 0; i < C::XPW; ++i) piece_x(i);
@@ -432,7 +434,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
     for (int i = 0; i < C::WPW; ++i) piece_w(i);
     end_w();
   }
-  waitvm<0>();
+  waitvm<C::WPW>();
   wait_lgkm0();
   barrier();
 #pragma unroll

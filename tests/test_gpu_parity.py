@@ -207,6 +207,35 @@ def test_pack_unit_scale_near_ties_exact(g, k):
     assert np.array_equal(q_or.astype(np.int64), expect)
 
 
+@pytest.mark.parametrize("g,k", [(1, 1024), (4, 2048), (16, 4096), (64, 4096), (256, 5120),
+                                 (256, 12288), (1024, 65536)])
+def test_pack_unit_scale_ties_exact_bf16(g, k):
+    """The same spike rows with bf16 input (the bf16 kernels form the first
+    butterfly stage from the packed pairs): values that bf16 holds exactly,
+    ties among them, codes exact."""
+    vals = np.array([127.0, 0.5, -0.5, 1.5, 2.5, -2.5, 126.5, -126.5, -127.0, 0.0, 3.5, 64.5,
+                     -100.5, 1.0, 2.0, 125.5])
+    want = np.array([127, 1, -1, 2, 3, -3, 127, -127, -127, 0, 4, 65, -101, 1, 2, 126])
+    ngroups = k // g
+    rows = 3
+    y = np.zeros((rows, k))
+    expect = np.zeros((rows, k), dtype=np.int64)
+    for r in range(rows):
+        for j in range(ngroups):
+            y[r, j * g + (r * 5 + j) % g] = vals[(j + r) % len(vals)]
+            expect[r, j * g + (r * 5 + j) % g] = want[(j + r) % len(vals)]
+    x = orc.rotate(y, g)
+    xt = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+    assert np.array_equal(xt.to(torch.float64).numpy(), x)  # bf16 holds X exactly
+    _say(f"pack unit-scale ties bf16 G={g} K={k}")
+    p = cr.pack_activations(xt.cuda(), g)
+    q, s = host(p.q), host(p.scale)
+    assert np.all(s == 1.0)
+    assert np.array_equal(q.astype(np.int64), expect)
+    q_or, _ = orc.pack_activations(x, g)
+    assert np.array_equal(q_or.astype(np.int64), expect)
+
+
 @pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("g,k", [(1, 1024), (16, 3072), (64, 3072), (256, 3072), (256, 12288),
                                  (16384, 16384)])
