@@ -167,11 +167,24 @@ def all_configs(args):
             for spec, qw in linears:
                 gl = w.gelu_chain
                 y = torch.empty((m, spec.n), dtype=torch.float32, device="cuda")
-                t = _time_ms(lambda: cr.linear(packed, qw, out=y, gelu=gl))
+                if gl:
+                    # the GELU epilogue's cost: alternate the launch with and
+                    # without it (same shape) and take medians
+                    tg, tp = [], []
+                    for _ in range(6):
+                        tg.append(_time_ms(lambda: cr.linear(packed, qw, out=y, gelu=True)))
+                        tp.append(_time_ms(lambda: cr.linear(packed, qw, out=y)))
+                    t, t_plain = statistics.median(tg), statistics.median(tp)
+                else:
+                    t = _time_ms(lambda: cr.linear(packed, qw, out=y))
                 tops = 2.0 * m * spec.n * k / (t * 1e-3) / 1e12
+                extra = {}
+                if gl:
+                    extra = {"us_without_gelu": round(t_plain * 1e3, 2),
+                             "gelu_overhead": round(t / t_plain - 1.0, 4)}
                 emit(workload=w.name, kernel="linear", linear=spec.name, m=m, n=spec.n, k=k,
                      group_size=g, gelu=gl, us=round(t * 1e3, 2), tops=round(tops, 1),
-                     mfma_frac=round(tops / PEAK_INT8_TOPS, 4))
+                     mfma_frac=round(tops / PEAK_INT8_TOPS, 4), **extra)
                 if w.gelu_chain:  # the down projection on this (float32) output
                     dspec, dqw = w.linears[1], qws[1]
                     hp = cr.pack_activations(y, g)

@@ -102,26 +102,28 @@ constexpr float kTinyRowScale = 0x1p64f;
 CR_DEVICE int clamp127(int q) { return max(-127, min(127, q)); }
 
 // GELU in its erf form, y Phi(y), with Phi the standard normal CDF.  For
-// either sign of y, y Phi(y) = max(y, 0) - |y| h with h = Phi(-|y|) =
-// erfc(|y| / sqrt 2) / 2.  h comes from Abramowitz & Stegun, Handbook of
-// Mathematical Functions, formula 7.1.26: for a >= 0,
-// erfc(a) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) e^{-a^2}, t = 1 / (1 + p a),
-// absolute error at most 1.5e-7.  The halving is folded into the
-// coefficients and 1/sqrt 2 into p and the exponent, which leaves eleven
-// full-rate operations plus the hardware reciprocal and base-2 exponential
-// per value (the form 0.5 y (1 + erf(y / sqrt 2)) takes three more).  The
+// either sign of y, y Phi(y) = max(y, 0) - |y| h with h = Phi(-|y|).  h is
+// 2^P(u), u = min(|y|, 6) / 3 - 1 in [-1, 1], with P the degree-7 polynomial
+// that gelu_fit.py fits to log2 Phi(-a) on [0, 6] (least squares at Chebyshev
+// nodes): the fit is within 5.7e-6 of log2 Phi(-a), so |y| |dh| stays below
+// 1e-6, and Phi(-6) < 1e-9 bounds what the clamp at 6 leaves out.  One
+// base-2 exponential and eleven full-rate operations per value (a
+// reciprocal-based erfc form needs a second transcendental operation); the
 // GEMM epilogue evaluates it for every output, where each vector
 // instruction takes issue time from the matrix core.
 CR_DEVICE float gelu_erf(float y) {
-  const float a = fabsf(y);
-  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.23164188826636f, a, 1.0f));  // p / sqrt 2
-  float q = __builtin_fmaf(t, 0.5307027145f, -0.7265760135f);  // a5 / 2, a4 / 2
-  q = __builtin_fmaf(t, q, 0.7107068705f);                     // a3 / 2
-  q = __builtin_fmaf(t, q, -0.142248368f);                     // a2 / 2
-  q = __builtin_fmaf(t, q, 0.127414796f);                      // a1 / 2
-  q *= t;
-  const float e = __builtin_amdgcn_exp2f(-0.72134752044448f * y * y);  // e^{-y^2 / 2}
-  return __builtin_fmaf(-a, q * e, fmaxf(y, 0.0f));
+  const float a = fminf(fabsf(y), 6.0f);
+  const float u = __builtin_fmaf(a, 0.33333334f, -1.0f);
+  float p = -0.0041326126f;
+  p = __builtin_fmaf(p, u, 0.016766453f);
+  p = __builtin_fmaf(p, u, -0.040761326f);
+  p = __builtin_fmaf(p, u, 0.09175151f);
+  p = __builtin_fmaf(p, u, -0.20396878f);
+  p = __builtin_fmaf(p, u, -6.0339985f);
+  p = __builtin_fmaf(p, u, -14.209558f);
+  p = __builtin_fmaf(p, u, -9.532935f);
+  const float h = __builtin_amdgcn_exp2f(p);
+  return __builtin_fmaf(-fabsf(y), h, fmaxf(y, 0.0f));
 }
 
 }  // namespace convrot

@@ -84,12 +84,14 @@ constexpr int kThreads = 256;  // 4 waves
 constexpr int kGroupM = 4;
 constexpr int kMinSteps = 3;   // K steps per tile at least (see the header comment)
 
-// Output modes.  kModeF32 scales each value as it is stored; the tile-end
-// modes turn the whole tile into float32 values at its end (and add the
-// adapters there), and only store them -- with GELU as well, which then
-// leaves the store-time VALU work to the erf alone (measurably faster than
-// scaling at store time too).
-enum { kModeF32 = 0, kModeI32 = 2, kModeTileEnd = 3, kModeTileEndGelu = 4 };
+// Output modes.  kModeF32 scales each value as it is stored, and
+// kModeF32Gelu applies the GELU there as well; the tile-end modes turn the
+// whole tile into float32 values at its end (and add the adapters there),
+// and only store them (through the GELU in kModeTileEndGelu).  Without
+// adapters, scaling at store time is the faster GELU form: the tile-end
+// conversion runs while the matrix cores wait, the store-time work under
+// the next tile's MFMAs.
+enum { kModeF32 = 0, kModeF32Gelu = 1, kModeI32 = 2, kModeTileEnd = 3, kModeTileEndGelu = 4 };
 
 template <int BN>
 struct Cfg {
@@ -184,10 +186,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
   using C = Cfg<BN>;
   constexpr int FM = C::FM, FN = C::FN, NV = C::NV, NG = C::NG, NSS = C::NSS;
   constexpr bool LORA = MODE == kModeTileEnd || MODE == kModeTileEndGelu;  // tile-end epilogue
-  constexpr bool GELU = MODE == kModeTileEndGelu;
+  constexpr bool GELU = MODE == kModeTileEndGelu || MODE == kModeF32Gelu;
   // Scales and bias applied when a value is stored (otherwise the pending
   // values are raw int32 results or finished float32 values).
-  constexpr bool SCALE_AT_STORE = MODE == kModeF32;
+  constexpr bool SCALE_AT_STORE = MODE == kModeF32 || MODE == kModeF32Gelu;
   __shared__ __attribute__((aligned(1024))) int8_t smem[C::LDS];
 
   const int lane = threadIdx.x & 63;
@@ -478,18 +480,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
       }
     }
     // The parked groups (the step's last NPK groups) of the last storing
-    // step, read from LDS one value per MFMA in the sub-step before the one
-    // that stores them.
+    // step, read from LDS one value per MFMA, PKL MFMAs before the one whose
+    // store writes it (enough to cover the LDS latency; a longer lead keeps
+    // more of them live in registers at once).
     int pk[C::NPK * NV];
     constexpr int PK0 = GPS - C::NPK;  // first parked group within the step
+    constexpr int PKL = 4;
     auto read_parked = [&](int kk, int idx) {  // reads issued under MFMA idx of sub-step kk
       if constexpr (SS == C::NSS - 1) {
 #pragma unroll
         for (int v = 0; v < C::NPK * NV; ++v) {
           const int g = PK0 + v / NV;            // group within the step
           const int store_kk = 1 + g / C::GSUB;  // sub-step that stores it
-          const int slot = ((g % C::GSUB) * NV + v % NV) * C::ST;  // its store slot
-          if (kk == store_kk - 1 && idx == slot % C::NMF) pk[v] = *park_slot(NG - C::NPK + v / NV, v % NV);
+          const int slot = ((g % C::GSUB) * NV + v % NV) * C::ST + C::ST - 1;  // MFMA of its store
+          const int at = store_kk * C::NMF + slot - PKL;  // position of the read
+          if (kk * C::NMF + idx == at) pk[v] = *park_slot(NG - C::NPK + v / NV, v % NV);
         }
       }
     };
@@ -836,7 +841,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     if (a.lora || a.gelu) return hipErrorInvalidValue;
     return launch_t<kBN, kModeI32>(p, stream);
   }
-  if (a.gelu) return launch_t<kBN, kModeTileEndGelu>(p, stream);  // ranks 0 without adapters
+  if (a.gelu && !a.lora) return launch_t<kBN, kModeF32Gelu>(p, stream);
+  if (a.gelu) return launch_t<kBN, kModeTileEndGelu>(p, stream);
   if (a.lora) return launch_t<kBN, kModeTileEnd>(p, stream);
   return launch_t<kBN, kModeF32>(p, stream);
 }

@@ -3,8 +3,9 @@
 Every entry point launches asynchronously on the caller's stream, allocates
 nothing and clears memory with kernels, never with a memset, so a caller
 may capture a whole layer step in a graph: the activation pack, grouped
-linears on the persistent GEMM, linears with adapters (down projection and
-the fused up projection) and a short-output linear on the split-K kernel.
+linears on the persistent GEMM (plain and with the GELU epilogue), linears
+with adapters (down projection and the fused up projection) and a
+short-output linear on the split-K kernel.
 
 Each replay runs on new input values copied into the captured input
 buffers, with eager launches and synchronisations between replays, and its
@@ -54,12 +55,13 @@ def _inputs():
 def _step(xa, xb, wa, wb, ads):
     pa = cr.pack_activations(xa, 256)
     plain = cr.linear_grouped(pa, wa)
+    plain_gelu = cr.linear_grouped(pa, wa[:2], gelu=True)  # GELU at store time, no adapters
     us = [cr.lora_down(xa, a, scale) for a, _, scale in ads]
     fused = cr.linear_lora(pa, wa, [(u, b) for u, (_, b, _) in zip(us, ads)] + [None], gelu=True)
     pb = cr.pack_activations(xb, 16)
     short = cr.linear(pb, wb)
     short_gelu = cr.linear(pb, wb, gelu=True)
-    return [pa.q, pa.scale, *plain, *us, *fused, pb.q, pb.scale, short, short_gelu]
+    return [pa.q, pa.scale, *plain, *plain_gelu, *us, *fused, pb.q, pb.scale, short, short_gelu]
 
 
 def _variant(x0, i):
