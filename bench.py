@@ -11,8 +11,12 @@ timed region starts.
 Prints one JSON line: value = effective INT8 TOPS of the whole step
 (2*M*N*K / step time, the pack included), plus the pack's HBM GB/s, the
 roofline of the dominant kernel (the GEMM) from HIP events recorded on the
-launch stream around every launch in the timed region, and the CPU oracle
-timed on a bounded sample of the same workload.
+launch stream around every 4th launch in the timed region, and the CPU
+oracle timed on a bounded sample of the same workload.  Measured before
+the warm-up steps and reported beside them: the pack alone (warm and
+cold), a plain copy of the pack's byte count, a register-only MFMA loop on
+the same operand codes (the matrix cores' ceiling under the power limit)
+and the GEMM alone over back-to-back launches.
 """
 
 from __future__ import annotations
@@ -434,15 +438,18 @@ def main():
 
     # Before the step loop: the pack alone (warm: back-to-back launches; cold:
     # after a 512 MB cache-flushing write), a plain copy of the same byte
-    # count, and the matrix cores' rate on these operand codes.  Besides their
-    # own figures these runs bring the shader clock to the steady state it
-    # holds under sustained work before the warm-up steps begin.
+    # count, the matrix cores' rate on these operand codes, and the grouped
+    # GEMM alone over 200 back-to-back launches.  Besides their own figures
+    # these runs (about 0.1 s) bring the shader clock to the state it holds
+    # under sustained work before the warm-up steps begin: from idle, the
+    # GEMM needs about 200 launches to settle.
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
     pack_avg_ms = _time_ms(lambda: cr.pack_activations(x, g, out=packed), reps=50)
     pack_cold_ms = _time_ms(lambda: cr.pack_activations(x, g, out=packed), reps=20, flush=flush)
     copy_warm_gbps, copy_cold_gbps = copy_ceiling(pack_bytes, flush)
     del flush
     mfma_loop_tops = mfma_ceiling(packed.q, qws[0].q)
+    gemm_alone_ms = _time_ms(lambda: cr.linear_grouped(packed, qws, outs=ys), reps=200)
     pack_gbps = pack_bytes / (pack_avg_ms * 1e-3) / 1e9
     pack_cold_gbps = pack_bytes / (pack_cold_ms * 1e-3) / 1e9
 
@@ -519,6 +526,7 @@ def main():
         "copy_gbps_warm": round(copy_warm_gbps, 1),
         "copy_gbps_cold": round(copy_cold_gbps, 1),
         "pack_frac_of_copy_cold": round(pack_cold_gbps / copy_cold_gbps, 4),
+        "gemm_us_back_to_back": round(gemm_alone_ms * 1e3, 3),
         "mfma_loop_tops": None if mfma_loop_tops is None else round(mfma_loop_tops, 1),
         "gemm_frac_of_mfma_loop": (None if mfma_loop_tops is None
                                    else round(gemm_tops / mfma_loop_tops, 4)),
