@@ -28,8 +28,9 @@
 //     one step ahead), Q_w in 3 stages (two steps ahead).  Each wave's 14
 //     loads of a step are spread one per ~3 MFMAs: a load that cannot issue
 //     also holds back the MFMAs behind it.  The buffer resources span the
-//     tile's valid rows, so rows past M or N and chunks past K read as zero
-//     (hardware range check) and need no clamping or clearing.  A tile has
+//     tile's valid rows, so rows past M or N read as zero (hardware range
+//     check) and need no clamping or clearing; so do the Q_w chunks past K,
+//     which zero whatever the Q_x chunks there hold.  A tile has
 //     at least 3 K steps (short K is padded with such zero chunks), so the
 //     load streams never run more than one tile ahead.
 //   * Everything a tile needs from the kernel arguments (buffer resources of
@@ -199,7 +200,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
   // into the kernel prologue, where they would stay live (and spill) for the
   // whole kernel.
   int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int G = gridDim.x;
+  // The grid size and the activation pointers, made opaque once: otherwise
+  // the compiler may reload them from the kernel arguments right before a K
+  // loop, and a scalar load in flight turns every LDS wait in that loop into
+  // a wait for all of them.
+  int G = gridDim.x;
+  const int8_t* qx = p.qx;
+  const float* sx = p.sx;
+  asm volatile("" : "+s"(G), "+s"(qx), "+s"(sx));
   const int slot = xcd_slot(blockIdx.x, G);
   const int ntiles = (p.total_tiles - slot + G - 1) / G;  // >= 1: grid <= tiles
   const int nk = p.nk;                                    // >= kMinSteps
@@ -213,17 +221,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
   // q & 1 = wave & 1 for every piece of a wave.  The two operands are loaded
   // as independent streams (Q_w runs one step further ahead); past the last
   // tile a stream repeats that tile into stages nobody reads any more.
+  //
+  // A load's byte offset is lane_off (the lane's row within the piece and its
+  // chunk, the same for every load of the launch) plus the piece's first row
+  // and the step's K offset, which are uniform and go into the instruction's
+  // scalar offset: no vector work per load or step.  The range check covers
+  // the sum of both offsets, so rows past the tile's last read zeros.  Past K
+  // (in a step that BK does not fit into K, and in the zero-padded steps of a
+  // short K) the Q_w lanes use an offset outside every resource and read
+  // zeros; the Q_x lanes there read the next row's bytes, which only ever
+  // meet those zeros.
   auto ld_chunk = [&]() { return (lane & 7) ^ (lane >> 3) ^ (wave & 1); };
-  auto ld_off = [&]() { return (lane >> 3) * K + ld_chunk() * 16; };  // < 8 * K <= 2^21
+  const unsigned lane_off = unsigned((lane >> 3) * K + ld_chunk() * 16);  // < 8 * K <= 2^21
+  // ... for the step that holds K's end (if BK does not divide K)
+  const unsigned w_part_off = ld_chunk() * 16 < K % C::BK ? lane_off : kOutOfRange;
   struct Stream {
     __amdgpu_buffer_rsrc_t rs, next;  // this tile's rows; the next tile's (set by its prologue)
     int ks, stage;
-    unsigned voff;  // this lane's offset in the current step, out of range past K
   };
   auto x_rsrc = [&](int t_it) {
     const TileInfo ti = tile_info<BN>(p, slot + t_it * G);
     const int rows = M - ti.m0 < kBM ? M - ti.m0 : kBM;
-    return buffer_rsrc(p.qx + (int64_t)ti.m0 * K, rows * K);
+    return buffer_rsrc(qx + (int64_t)ti.m0 * K, rows * K);
   };
   auto w_rsrc = [&](int t_it) {
     const TileInfo ti = tile_info<BN>(p, slot + t_it * G);
@@ -231,27 +250,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
     const int rows = sg.n - ti.n0 < BN ? sg.n - ti.n0 : BN;
     return buffer_rsrc(sg.qw + (int64_t)ti.n0 * K, rows * K);
   };
-  Stream xs{x_rsrc(0), x_rsrc(0), 0, 0, kOutOfRange};
-  Stream ws{w_rsrc(0), w_rsrc(0), 0, 0, kOutOfRange};
-  auto begin_x = [&]() {
-    const int k0 = xs.ks * C::BK;
-    xs.voff = (k0 + ld_chunk() * 16 < K) ? unsigned(ld_off() + k0) : kOutOfRange;
-  };
+  Stream xs{x_rsrc(0), x_rsrc(0), 0, 0};
+  Stream ws{w_rsrc(0), w_rsrc(0), 0, 0};
+  unsigned w_voff = lane_off;  // Q_w lane offset of the step being loaded
   auto begin_w = [&]() {
     const int k0 = ws.ks * C::BK;
-    ws.voff = (k0 + ld_chunk() * 16 < K) ? unsigned(ld_off() + k0) : kOutOfRange;
+    w_voff = k0 + C::BK <= K ? lane_off : k0 < K ? w_part_off : kOutOfRange;
   };
   auto piece_x = [&](int i) {
     int8_t* dst = smem + xs.stage * C::XSTAGE + (wave + 4 * i) * 1024;
-    const unsigned off = xs.voff + unsigned((wave + 4 * i) * 8 * K);
+    const int soff = xs.ks * C::BK + (wave + 4 * i) * 8 * K;
     const __amdgpu_buffer_rsrc_t rs = xs.rs;  // (a local: the host pass rejects a member)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, lane_off, soff, 0, 0);
   };
   auto piece_w = [&](int i) {
     int8_t* dst = smem + C::WOFF + ws.stage * C::WSTAGE + (wave + 4 * i) * 1024;
-    const unsigned off = ws.voff + unsigned((wave + 4 * i) * 8 * K);
+    const int soff = ws.ks * C::BK + (wave + 4 * i) * 8 * K;
     const __amdgpu_buffer_rsrc_t rs = ws.rs;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, w_voff, soff, 0, 0);
   };
   auto end_x = [&]() {
     xs.stage ^= 1;
@@ -269,6 +285,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
   };
   // s_x | s_w | b of tile t_it into parameter buffer t_it % 2.  Float f of a
   // buffer is loaded by wave (f / 64) % 4, lane f % 64 (padding loads s_x[0]).
+  // The section boundaries are multiples of 64, so each wave's 64 floats come
+  // from one array: a buffer load through a wave-uniform resource.  (A global
+  // load into LDS would do the same work, but the compiler counts it as a flat
+  // access still in flight and then waits for all LDS reads, lgkmcnt(0),
+  // wherever the K loop needs only the oldest fragments.)
+  static_assert(kBM % 64 == 0 && BN % 64 == 0, "a wave's parameter floats share one array");
   auto issue_params = [&](int t_it) {
     const TileInfo ti = tile_info<BN>(p, slot + t_it * G);
     const float* sw = p.seg[ti.s].sw;
@@ -277,19 +299,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
     int8_t* par = smem + C::PAR0 + (t_it & 1) * C::PARB;
 #pragma unroll
     for (int rd = 0; rd < C::PR; ++rd) {
-      const int f0 = rd * 256 + wave * 64;
+      // The resource covers the tile's own rows or columns (at most 256
+      // floats); idx is relative to the tile's first one.
+      const int f0 = rd * 256 + wave * 64;  // uniform
       const int f = f0 + lane;
-      const float* src = p.sx;
-      if (f < kBM) {
-        const int m = ti.m0 + f;
-        src = p.sx + (m < M ? m : M - 1);
-      } else if (f < kBM + 2 * BN) {
-        const bool is_w = f < kBM + BN;
-        int n = ti.n0 + (is_w ? f - kBM : f - kBM - BN);
-        n = n < n_lim ? n : n_lim;
-        src = (is_w || !bias) ? sw + n : bias + n;
+      const float* src = sx;
+      int bytes = 4, idx = 0;
+      if (f0 < kBM) {
+        const int last = M - 1 - ti.m0;  // >= 0: the tile has rows
+        src = sx + ti.m0;
+        bytes = (last < kBM ? last + 1 : kBM) * 4;
+        idx = f < last ? f : last;
+      } else if (f0 < kBM + 2 * BN) {
+        const bool is_w = f0 < kBM + BN;
+        const int last = n_lim - ti.n0;  // >= 0: the tile has columns
+        const int c = is_w ? f - kBM : f - kBM - BN;
+        src = ((is_w || !bias) ? sw : bias) + ti.n0;
+        bytes = (last < BN ? last + 1 : BN) * 4;
+        idx = c < last ? c : last;
       }
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(par + f0 * 4), 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(src, bytes), (lds_void*)(par + f0 * 4),
+                                               4, idx * 4, 0, 0, 0);
     }
   };
 
@@ -425,7 +455,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
   // pieces of step 1.  Only step 0's operands are waited for here: Q_w of
   // step 1 (the last WPW loads) lands under step 0, whose closing wait
   // covers it.
-  begin_x();
 #pragma unroll
   for (int i = 0; i < C::XPW; ++i) piece_x(i);
   end_x();
@@ -443,7 +472,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
   for (int f = 0; f < FM; ++f) read_x(smem, f, 0);
 #pragma unroll
   for (int f = 0; f < FN; ++f) read_w(smem + C::WOFF, 0, f, 0);
-  begin_x();
 #pragma unroll
   for (int i = 0; i < C::XT; ++i) piece_x(i);
 
@@ -573,7 +601,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
     waitvm<C::WPW + NST>();
     wait_lgkm0();
     barrier();  // the next stages are readable by all, this step's are free
-    begin_x();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int idx = 2; idx < C::NMF; ++idx) {
