@@ -103,25 +103,22 @@ CR_DEVICE int clamp127(int q) { return max(-127, min(127, q)); }
 
 // GELU in its erf form, y Phi(y), with Phi the standard normal CDF.  For
 // either sign of y, y Phi(y) = max(y, 0) - |y| h with h = Phi(-|y|).  h is
-// 2^P(u), u = min(|y|, 6) / 3 - 1 in [-1, 1], with P the degree-7 polynomial
-// that gelu_fit.py fits to log2 Phi(-a) on [0, 6] (least squares at Chebyshev
-// nodes): the fit is within 5.7e-6 of log2 Phi(-a), so |y| |dh| stays below
-// 1e-6, and Phi(-6) < 1e-9 bounds what the clamp at 6 leaves out.  One
-// base-2 exponential and eleven full-rate operations per value (a
-// reciprocal-based erfc form needs a second transcendental operation); the
-// GEMM epilogue evaluates it for every output, where each vector
-// instruction takes issue time from the matrix core.
+// 2^P(t), t = min(|y|, 6) / 6, with P the degree-5 polynomial that
+// gelu_fit.py fits to log2 Phi(-a) on [0, 6], weighted by how much an error
+// of P moves the GELU value (|y| h ln2 per unit, relative to max(1, |y|)):
+// the float32 result stays within 3.3e-7 max(1, |y|) of y Phi(y), and
+// Phi(-6) < 1e-9 bounds what the clamp at 6 leaves out.  Nine full-rate
+// vector operations and one base-2 exponential per value (t is a single
+// multiply whose output clamp bit does the min); the GEMM epilogue evaluates
+// it for every output, and each vector instruction costs matrix-core time.
 CR_DEVICE float gelu_erf(float y) {
-  const float a = fminf(fabsf(y), 6.0f);
-  const float u = __builtin_fmaf(a, 0.33333334f, -1.0f);
-  float p = -0.0041326126f;
-  p = __builtin_fmaf(p, u, 0.016766453f);
-  p = __builtin_fmaf(p, u, -0.040761326f);
-  p = __builtin_fmaf(p, u, 0.09175151f);
-  p = __builtin_fmaf(p, u, -0.20396878f);
-  p = __builtin_fmaf(p, u, -6.0339985f);
-  p = __builtin_fmaf(p, u, -14.209558f);
-  p = __builtin_fmaf(p, u, -9.532935f);
+  const float t = fminf(fmaxf(fabsf(y) * 0.16666667f, 0.0f), 1.0f);
+  float p = -3.9505641f;
+  p = __builtin_fmaf(p, t, 9.483913f);
+  p = __builtin_fmaf(p, t, -11.315078f);
+  p = __builtin_fmaf(p, t, -16.538921f);
+  p = __builtin_fmaf(p, t, -6.9062366f);
+  p = __builtin_fmaf(p, t, -1.0000027f);
   const float h = __builtin_amdgcn_exp2f(p);
   return __builtin_fmaf(-fabsf(y), h, fmaxf(y, 0.0f));
 }
