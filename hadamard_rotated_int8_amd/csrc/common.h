@@ -20,6 +20,7 @@ constexpr int kVmMax = 63;     // largest vmcnt a wait can name
 // Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format).
 constexpr int kBufferWord3 = 0x00020000;
 constexpr unsigned kOutOfRange = 0x80000000u;  // an offset past every resource
+constexpr int kNonTemporal = 2;  // cache-policy bits of a buffer access: nt (streaming)
 
 // A raw buffer resource over [base, base + bytes): loads at offsets past the
 // end return zero (the hardware range check).

@@ -380,7 +380,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
   int pd_sxo = 0;              // LDS offset of this lane's s_x for group 0
   int pd_m0w = 0, pd_n0w = 0;  // uniform parts: m0 + wm*128, n0 + wn*BN/2
   int pd_fast = 0;             // interior tile with a row stride that fits the fast path
-  unsigned pd_voff = 0;        // lane part of a fast-path store address, in bytes
+  unsigned pd_voff = 0;        // lane part of a fast-path store offset, in bytes
+  __amdgpu_buffer_rsrc_t pd_rs = buffer_rsrc(nullptr, 0);  // fast path: the wave's 128 rows
   float* pd_y = nullptr;
   int64_t pd_ldy = 0;
   int pd_has_b = 0;             // the pending tile's weight has a bias
@@ -424,30 +425,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
 #pragma unroll
     for (int e = 0; e < NV; ++e) store_value(q, e, sx, yrow, m);
   };
-  // Fast path (interior tiles): the address is a uniform row base plus this
-  // lane's fixed 32-bit offset (4*(lane/32) rows and lane%32 columns).
+  // Fast path (interior tiles): non-temporal buffer stores through a
+  // resource over the wave's 128 rows; the row's byte offset is uniform (the
+  // scalar offset), the lane's (4*(lane/32) rows, lane%32 columns) is fixed,
+  // and the column block goes into the immediate offset.  No address
+  // arithmetic per store beyond one scalar add.
   auto group_rel = [&](int q) {  // row of group q relative to m0 + wm*128
     return (q >> 3) * 32 + 8 * ((q >> 1) & 3) + 2 * (q & 1);
   };
-  auto group_base_from = [&](int m0w, int q) {
-    return reinterpret_cast<char*>(pd_y) + ((int64_t)(m0w + group_rel(q)) * pd_ldy + pd_n0w) * 4;
-  };
-  auto group_base = [&](int q) { return group_base_from(pd_m0w, q); };
-  auto store_raw_with = [&](int raw, char* base, f32x2 sx, int e, float sw, float b) {
+  auto group_off = [&](int q) { return group_rel(q) * (int)pd_ldy * 4; };  // < 2^31 (pd_fast)
+  auto store_raw_with = [&](int raw, int goff, f32x2 sx, int e, float sw, float b) {
     const int j = e >> 1, rr = e & 1;
     const float v = scaled_with(raw, sx[rr], sw, b);
-    char* row = base + rr * pd_ldy * 4;
-    __builtin_nontemporal_store(v, reinterpret_cast<float*>(row + pd_voff + j * 128));
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), pd_rs, pd_voff + j * 128,
+                                          goff + rr * (int)pd_ldy * 4, kNonTemporal);
   };
-  auto store_raw = [&](int raw, char* base, f32x2 sx, int e) {
-    store_raw_with(raw, base, sx, e, pd_sw[e >> 1], pd_b[e >> 1]);
+  auto store_raw = [&](int raw, int goff, f32x2 sx, int e) {
+    store_raw_with(raw, goff, sx, e, pd_sw[e >> 1], pd_b[e >> 1]);
   };
-  auto store_fast = [&](int q, char* base, f32x2 sx, int e) { store_raw(pend_get(q, e), base, sx, e); };
+  auto store_fast = [&](int q, int goff, f32x2 sx, int e) { store_raw(pend_get(q, e), goff, sx, e); };
   auto store_group_fast = [&](int q) {
     const f32x2 sx = read_group_sx(q);
-    char* base = group_base(q);
+    const int goff = group_off(q);
 #pragma unroll
-    for (int e = 0; e < NV; ++e) store_fast(q, base, sx, e);
+    for (int e = 0; e < NV; ++e) store_fast(q, goff, sx, e);
   };
 
   // ------------------------------------------------------------ prologue
@@ -573,7 +574,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
             const int q = GPS * SS + g;
             const int raw = q >= NG - C::NPK ? pk[(q - (NG - C::NPK)) * NV + e]
                                              : pend[q < NG - C::NPK ? q : 0][e];
-            store_raw_with(raw, group_base(q), gsx[sn / NV], e, gsw[e >> 1], gb[e >> 1]);
+            store_raw_with(raw, group_off(q), gsx[sn / NV], e, gsw[e >> 1], gb[e >> 1]);
           }
           if (kk == 1 && idx == C::NMF - 1) read_gsx(2);
           read_parked(kk, idx);
@@ -785,8 +786,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
     pd_interior = (ti.m0 + kBM <= M) && (ti.n0 + BN <= sg.n);
     pd_m0w = ti.m0 + (wave >> 1) * 128;
     pd_n0w = ti.n0 + (wave & 1) * C::WN;
-    pd_fast = pd_interior && sg.ldy < (int64_t(1) << 26);
+    // (128 rows of a stride below 2^22 floats: every offset fits 31 bits)
+    pd_fast = pd_interior && sg.ldy < (int64_t(1) << 22);
     pd_voff = unsigned((4 * (lane >> 5)) * (int)(pd_fast ? sg.ldy : 0) + (lane & 31)) * 4u;
+    pd_rs = buffer_rsrc(pd_y + (int64_t)pd_m0w * pd_ldy + pd_n0w, pd_fast ? 128 * (int)pd_ldy * 4 : 0);
     pd_has_b = sg.bias != nullptr;
   }
   // The last tile.
