@@ -41,6 +41,7 @@ PEAK_HBM_GBPS = 8000.0    # MI355X HBM3E, 8 TB/s
 GEMM_SOURCE = os.path.join(ROOT, "hadamard_rotated_int8_amd", "csrc", "gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_qkv_4096x3072x9216_traffic.json")
 CALIBRATION_BYTES = 256 * 1024 * 1024  # the plain copy whose counters scale FETCH/WRITE_SIZE
+WARM_MS = 25.0  # sustained launches before a back-to-back timing (clock settling)
 
 
 def parse():
@@ -79,14 +80,25 @@ def gemm_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
-def _time_ms(fn, reps=20, flush=None):
+def _time_ms(fn, reps=20, flush=None, warm_ms=WARM_MS):
     """Average ms per call over back-to-back launches, or the median of single
-    launches each after a cache-flushing write when ``flush`` is given."""
+    launches each after a cache-flushing write when ``flush`` is given.
+    Back-to-back timings first run the call for about ``warm_ms`` ms: after
+    idle time or a short kernel the clock needs some 20 ms of sustained work
+    to settle, and the first launches run slower."""
     import torch
 
     fn()
     torch.cuda.synchronize()
     if flush is None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        for _ in range(min(5000, int(warm_ms / max(e0.elapsed_time(e1), 1e-3)))):
+            fn()
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):

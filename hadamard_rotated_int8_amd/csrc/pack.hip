@@ -92,6 +92,25 @@ CR_DEVICE float h4_wave(float x) {
   return __builtin_fmaf(-2.f, c, s);
 }
 
+// Maximum over the wave of a float that is non-negative and not NaN in every
+// lane (a lane's own fmaxf of |x| drops NaNs): such floats order as their
+// bit patterns do as unsigned integers, so the cross-lane steps are integer
+// maxima, four of them fused with DPP lane moves (quads, then rotations
+// inside rows of 16) and two across rows and wave halves by the permlane
+// swaps; no LDS round trips on the row's critical path.
+CR_DEVICE float wave_max_nonneg(float x) {
+  unsigned v = __float_as_uint(x);
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, kDppQuadSwap1, 0xF, 0xF, false));
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, kDppQuadSwap2, 0xF, 0xF, false));
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowRor4, 0xF, 0xF, false));
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowRor8, 0xF, 0xF, false));
+  const auto rows = __builtin_amdgcn_permlane16_swap(v, v, false, false);  // rows 2i <-> 2i+1
+  v = max((unsigned)rows[0], (unsigned)rows[1]);
+  const auto halves = __builtin_amdgcn_permlane32_swap(v, v, false, false);  // lanes 0-31 <-> 32-63
+  v = max((unsigned)halves[0], (unsigned)halves[1]);
+  return __uint_as_float(v);
+}
+
 // Thread t owns chunk (t with bit 2 replaced by bit2 ^ bit3) of each block of
 // T chunks, which realises the lane -> digit map used by h4_row.  It permutes
 // chunks only inside aligned groups of 16 lanes, so loads stay coalesced.
@@ -291,8 +310,7 @@ __global__ __launch_bounds__(1024) void pack_kernel(const InT* __restrict__ x, i
       load_rotate_segment<InT, CPT>(xr, seg, nch, log4g, v, lds_buf, t, T);
       mx = fmaxf(mx, local_absmax<CPT>(v));
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    mx = wave_max_nonneg(mx);
     if (lane == 0) wave_max[wave] = mx;
     __syncthreads();
     mx = wave_max[0];
@@ -493,8 +511,7 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const InT* __restrict__ 
     for (int c = 0; c < CPL; ++c)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(v[c][e]));
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    mx = wave_max_nonneg(mx);
     bool tiny;
     float r;
     const float s = row_scale(mx, log4g, r, tiny);
@@ -615,8 +632,7 @@ __global__ __launch_bounds__(256) void pack_rows_lds_kernel(const InT* __restric
     for (int c = 0; c < CPL; ++c)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(t[c][e]));
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    mx = wave_max_nonneg(mx);
     if constexpr (WPR > 1) {
       if (lane == 0) red[it & 1][wv] = mx;
       __syncthreads();  // red[it & 1] is rewritten two rows later, after another barrier
