@@ -14,9 +14,10 @@ roofline of the dominant kernel (the GEMM) from HIP events recorded on the
 launch stream around every 4th launch in the timed region, and the CPU
 oracle timed on a bounded sample of the same workload.  Measured before
 the warm-up steps and reported beside them: the pack alone (warm and
-cold), a plain copy of the pack's byte count, a register-only MFMA loop on
-the same operand codes (the matrix cores' ceiling under the power limit)
-and the GEMM alone over back-to-back launches.
+cold), an HBM stream of the pack's bytes in its read:write mix (HBM's
+ceiling for such a pass), a register-only MFMA loop on the same operand
+codes (the matrix cores' ceiling under the power limit) and the GEMM alone
+over back-to-back launches.
 """
 
 from __future__ import annotations
@@ -118,20 +119,17 @@ def _time_ms(fn, reps=20, flush=None, warm_ms=WARM_MS):
     return float(np.median(ts))
 
 
-def copy_beside(nbytes, pack_warm_ms, pack_cold_ms, flush):
-    """A plain device copy moving the pack's byte count (reads and writes
-    nbytes / 2 each), warm and cold, and the pack's time as a fraction of it."""
-    import torch
-
-    half = nbytes // 2 // 4
-    src = torch.ones(half, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    warm = _time_ms(lambda: dst.copy_(src))
-    cold = _time_ms(lambda: dst.copy_(src), reps=10, flush=flush)
-    del src, dst
-    return {"copy_us_warm": round(warm * 1e3, 2), "copy_us_cold": round(cold * 1e3, 2),
-            "copy_over_pack_warm": round(warm / pack_warm_ms, 4),
-            "copy_over_pack_cold": round(cold / pack_cold_ms, 4)}
+def stream_beside(m, k, in_bytes, pack_warm_ms, pack_cold_ms, flush):
+    """The HBM stream kernel moving the pack's bytes in the pack's read:write
+    mix (stream_ceiling), warm and cold, and its time over the pack's (1.0:
+    the pack moves its bytes as fast as the stream)."""
+    r = stream_ceiling(m, k, in_bytes, flush)
+    if r is None:
+        return {}
+    warm, cold, _, _ = r
+    return {"stream_us_warm": round(warm * 1e3, 2), "stream_us_cold": round(cold * 1e3, 2),
+            "stream_over_pack_warm": round(warm / pack_warm_ms, 4),
+            "stream_over_pack_cold": round(cold / pack_cold_ms, 4)}
 
 
 def all_configs(args):
@@ -176,7 +174,7 @@ def all_configs(args):
                  us_warm=round(warm * 1e3, 2), us_cold=round(cold * 1e3, 2),
                  gbps_cold=round(pbytes / (cold * 1e-3) / 1e9, 1),
                  hbm_frac_cold=round(pbytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                 **copy_beside(pbytes, warm, cold, flush))
+                 **stream_beside(m, k, xb, warm, cold, flush))
             linears = list(zip(w.linears, qws))
             if w.gelu_chain:
                 linears = linears[:1]
@@ -211,7 +209,7 @@ def all_configs(args):
                          us_warm=round(hwarm * 1e3, 2), us_cold=round(hcold * 1e3, 2),
                          gbps_cold=round(hbytes / (hcold * 1e-3) / 1e9, 1),
                          hbm_frac_cold=round(hbytes / (hcold * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                         **copy_beside(hbytes, hwarm, hcold, flush))
+                         **stream_beside(m, spec.n, 4, hwarm, hcold, flush))
                     yd = torch.empty((m, dspec.n), dtype=torch.float32, device="cuda")
                     td = _time_ms(lambda: cr.linear(hp, dqw, out=yd))
                     dtops = 2.0 * m * dspec.n * spec.n / (td * 1e-3) / 1e12
@@ -366,6 +364,10 @@ def _ceiling_lib():
     f.restype = ctypes.c_int64
     f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
                   ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    f = lib.convrot_ceiling_stream
+    f.restype = ctypes.c_int32
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_void_p]
     return lib
 
 
@@ -398,18 +400,36 @@ def mfma_ceiling(qa, qb, reps=5):
     return ops / (float(np.median(ts[1:])) * 1e-3) / 1e12
 
 
-def copy_ceiling(nbytes, flush, reps=20):
-    """GB/s of a plain device copy that reads and writes nbytes / 2 each (the
-    pack's algorithmic byte count), warm and after a cache-flushing write."""
+def stream_ceiling(m, k, in_bytes, flush, reps=20):
+    """The HBM ceiling for a pack of an [m, k] input of in_bytes per element:
+    the measurement library's stream kernel reads in_bytes * m * k and writes
+    m * k bytes (the pack's bytes but the 4 per row of its scales, in its
+    read:write mix) with non-temporal 16-byte accesses.  Returns (warm ms,
+    cold ms, warm GB/s, cold GB/s) at the best of four grid sizes, warm =
+    back-to-back launches, cold = single launches after a cache-flushing
+    write; None without the measurement library."""
     import torch
 
-    half = nbytes // 2 // 4
-    src = torch.ones(half, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    warm = _time_ms(lambda: dst.copy_(src), reps=reps)
-    cold = _time_ms(lambda: dst.copy_(src), reps=reps, flush=flush)
-    moved = 2 * half * 4
-    return moved / (warm * 1e-3) / 1e9, moved / (cold * 1e-3) / 1e9
+    lib = _ceiling_lib()
+    if lib is None:
+        return None
+    dst_bytes = m * k // 16 * 16
+    src = torch.ones(dst_bytes * in_bytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty(dst_bytes // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def launch(grid):
+        if lib.convrot_ceiling_stream(src.data_ptr(), dst.data_ptr(), dst_bytes, in_bytes, grid,
+                                      stream) != 0:
+            raise RuntimeError("stream ceiling kernel refused its arguments")
+
+    best = min((_time_ms(lambda: launch(cus * w), reps=reps), cus * w) for w in (2, 4, 8, 16))
+    warm, grid = best
+    cold = _time_ms(lambda: launch(grid), reps=reps, flush=flush)
+    del src, dst
+    moved = dst_bytes * (in_bytes + 1)
+    return warm, cold, moved / (warm * 1e-3) / 1e9, moved / (cold * 1e-3) / 1e9
 
 
 def main():
@@ -449,8 +469,8 @@ def main():
     pack_bytes = m * k * (2 if x.dtype == torch.bfloat16 else 4) + m * k + 4 * m
 
     # Before the step loop: the pack alone (warm: back-to-back launches; cold:
-    # after a 512 MB cache-flushing write), a plain copy of the same byte
-    # count, the matrix cores' rate on these operand codes, and the grouped
+    # after a 512 MB cache-flushing write), an HBM stream of the same bytes in
+    # the same read:write mix, the matrix cores' rate on these operand codes, and the grouped
     # GEMM alone over 200 back-to-back launches.  Besides their own figures
     # these runs (about 0.1 s) bring the shader clock to the state it holds
     # under sustained work before the warm-up steps begin: from idle, the
@@ -458,7 +478,7 @@ def main():
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
     pack_avg_ms = _time_ms(lambda: cr.pack_activations(x, g, out=packed), reps=50)
     pack_cold_ms = _time_ms(lambda: cr.pack_activations(x, g, out=packed), reps=20, flush=flush)
-    copy_warm_gbps, copy_cold_gbps = copy_ceiling(pack_bytes, flush)
+    stream = stream_ceiling(m, k, 2 if x.dtype == torch.bfloat16 else 4, flush)
     del flush
     mfma_loop_tops = mfma_ceiling(packed.q, qws[0].q)
     gemm_alone_ms = _time_ms(lambda: cr.linear_grouped(packed, qws, outs=ys), reps=200)
@@ -535,9 +555,10 @@ def main():
         "pack_us_cold": round(pack_cold_ms * 1e3, 3),
         "pack_gbps_cold": round(pack_cold_gbps, 1),
         "pack_hbm_frac_cold": round(pack_cold_gbps / PEAK_HBM_GBPS, 4),
-        "copy_gbps_warm": round(copy_warm_gbps, 1),
-        "copy_gbps_cold": round(copy_cold_gbps, 1),
-        "pack_frac_of_copy_cold": round(pack_cold_gbps / copy_cold_gbps, 4),
+        "stream_gbps_warm": None if stream is None else round(stream[2], 1),
+        "stream_gbps_cold": None if stream is None else round(stream[3], 1),
+        "pack_frac_of_stream_warm": None if stream is None else round(pack_gbps / stream[2], 4),
+        "pack_frac_of_stream_cold": None if stream is None else round(pack_cold_gbps / stream[3], 4),
         "gemm_us_back_to_back": round(gemm_alone_ms * 1e3, 3),
         "mfma_loop_tops": None if mfma_loop_tops is None else round(mfma_loop_tops, 1),
         "gemm_frac_of_mfma_loop": (None if mfma_loop_tops is None

@@ -1,5 +1,6 @@
-// Measurement kernel for the INT8 GEMM's roofline (not on the hot path; built
-// into libconvrot_ceiling.so, which only the benchmark loads).
+// Measurement kernels for the hot path's rooflines (not on the hot path; built
+// into libconvrot_ceiling.so, which only the benchmark loads): the matrix
+// cores' rate for the INT8 GEMM and HBM's for the activation pack.
 //
 // A register-only loop of v_mfma_i32_32x32x32_i8 in the GEMM's per-wave shape:
 // one workgroup of 4 waves per CU (one wave per SIMD), each wave keeping a
@@ -11,6 +12,14 @@
 // cores sustain, depends on the operand bits.  No loads, LDS traffic or
 // stores run inside the loop, so its rate is the matrix cores' ceiling for
 // this operand data at the clock the chip holds under it.
+//
+// A streaming pass with the pack's read:write mix: every 16-byte chunk of the
+// destination receives the XOR of R source chunks (R = 2 for bf16 input and
+// int8 output, 4 for float32 input), with non-temporal 16-byte loads and
+// stores, grid-stride, each lane holding the loads of two destination chunks
+// in flight before it stores them.  No arithmetic to speak of, so its rate is
+// what HBM delivers to a pass that moves the pack's bytes in the pack's
+// proportions.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -71,7 +80,54 @@ __global__ __launch_bounds__(256, 1) void mfma_loop_kernel(const int8_t* a, int6
   sink[int64_t(wave) * 64 + lane] = r;
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Source plane j (j < R) holds chunks j * n16 .. j * n16 + n16 - 1, so every
+// load instruction of a wave reads 1 KB contiguous.
+template <int R>
+__global__ __launch_bounds__(256) void stream_kernel(const u32x4* __restrict__ src,
+                                                    u32x4* __restrict__ dst, int64_t n16) {
+  constexpr int kInFlight = 2;  // destination chunks per lane and round
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += kInFlight * stride) {
+    u32x4 v[kInFlight][R];
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) {
+      const int64_t c = i + u * stride;
+#pragma unroll
+      for (int j = 0; j < R; ++j)
+        v[u][j] = c < n16 ? __builtin_nontemporal_load(src + j * n16 + c) : u32x4{};
+    }
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) {
+      const int64_t c = i + u * stride;
+      u32x4 x = v[u][0];
+#pragma unroll
+      for (int j = 1; j < R; ++j) x ^= v[u][j];
+      if (c < n16) __builtin_nontemporal_store(x, dst + c);
+    }
+  }
+}
+
 }  // namespace
+
+extern "C" int32_t convrot_ceiling_stream(const void* src, void* dst, int64_t dst_bytes,
+                                          int32_t ratio, int32_t grid, void* stream) {
+  if (!src || !dst || dst_bytes < 16 || dst_bytes % 16) return -1;
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) return -1;
+  if (grid < 1 || grid > 65536) return -1;
+  const u32x4* s = static_cast<const u32x4*>(src);
+  u32x4* d = static_cast<u32x4*>(dst);
+  const int64_t n16 = dst_bytes / 16;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (ratio) {
+    case 1: hipLaunchKernelGGL(stream_kernel<1>, dim3(grid), dim3(256), 0, st, s, d, n16); break;
+    case 2: hipLaunchKernelGGL(stream_kernel<2>, dim3(grid), dim3(256), 0, st, s, d, n16); break;
+    case 4: hipLaunchKernelGGL(stream_kernel<4>, dim3(grid), dim3(256), 0, st, s, d, n16); break;
+    default: return -1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
 
 extern "C" int64_t convrot_ceiling_mfma_i8(const int8_t* a, int64_t lda, int64_t rows_a,
                                            const int8_t* b, int64_t ldb, int64_t rows_b,

@@ -40,14 +40,24 @@ def test_library_exports_every_declared_function():
         assert hasattr(L, name), name
 
 
-def test_ceiling_library_exports_its_declared_function():
-    """libconvrot_ceiling.so (the benchmark's measurement kernel) exports what
+def test_ceiling_library_exports_its_declared_functions():
+    """libconvrot_ceiling.so (the benchmark's measurement kernels) exports what
     include/convrot_ceiling.h declares, and refuses bad arguments on the host."""
     text = open(os.path.join(ROOT, "include", "convrot_ceiling.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = sorted(set(re.findall(r"\b(convrot_\w+)\s*\(", text)))
-    assert names == ["convrot_ceiling_mfma_i8"]
+    assert names == ["convrot_ceiling_mfma_i8", "convrot_ceiling_stream"]
     L = ctypes.CDLL(os.path.join(ROOT, "hadamard_rotated_int8_amd", "libconvrot_ceiling.so"))
+    s = L.convrot_ceiling_stream
+    s.restype = ctypes.c_int32
+    s.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_void_p]
+    assert s(None, FAKE, 1024, 2, 1, None) == -1      # null source
+    assert s(FAKE, FAKE, 1000, 2, 1, None) == -1      # not a multiple of 16 bytes
+    assert s(FAKE, FAKE, 0, 2, 1, None) == -1         # nothing to move
+    assert s(FAKE, FAKE, 1024, 3, 1, None) == -1      # ratio not 1, 2 or 4
+    assert s(FAKE, FAKE, 1024, 2, 0, None) == -1      # no workgroups
+    assert s(FAKE + 8, FAKE, 1024, 2, 1, None) == -1  # misaligned
     f = L.convrot_ceiling_mfma_i8
     f.restype = ctypes.c_int64
     f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
