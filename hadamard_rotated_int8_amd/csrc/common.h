@@ -94,6 +94,19 @@ CR_DEVICE int code_of_clamped(float x, float r) {
   return (int)__builtin_amdgcn_fmed3f(f, -127.0f, 127.0f);
 }
 
+// The code decision for a row whose multiplier r has at least 9 significant
+// bits (no_exact_ties(r)): x r is then never exactly a half-integer for
+// |x r| <= 127.5 (that needs odd(x) odd(r) = |2k + 1| <= 255, and the odd
+// part of r's significand is at least 256), so rounding the exact product to
+// nearest even is rounding it half away from zero, for every x.  The fused
+// multiply-add RN(x r + 1.5 2^23) does that rounding and leaves the integer
+// in the low mantissa bits in two's complement: the low byte of the result
+// is the int8 code (callers use that byte only).  One operation per code.
+CR_DEVICE int code_bits_rne(float x, float r) {
+  return __float_as_int(__builtin_fmaf(x, r, 0x1.8p23f));
+}
+CR_DEVICE bool no_exact_ties(float r) { return (__float_as_uint(r) & 0xFFFFu) != 0u; }
+
 // Rows whose absmax is below kTinyRowMax take the pre-scaled path: x and the
 // scale are both multiplied by 2^64 (exact), so 1/s cannot overflow float32
 // (it would for s below 2^-128), and the codes are clamped.

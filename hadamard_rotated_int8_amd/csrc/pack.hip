@@ -23,12 +23,16 @@
 //     that of the normalised butterfly;
 //   * the row absmax is reduced across lanes and then across waves in LDS;
 //   * the code decision is made in float32: s = m/127 (IEEE division) and
-//     r = RN(1/s) once per row, then per value one fused multiply-add,
-//     trunc(RN(x r + copysign(0.5 - 2^-25, x))): round half away from zero of
-//     x r (exact for s = 1; otherwise equal to round(x / s) except within a
-//     few ulp of a half-integer); rows with a tiny absmax are pre-scaled by
-//     2^64 so that 1/s cannot overflow; the int8 codes leave as 16-byte
-//     stores.
+//     r = RN(1/s) once per row, then per value a code.  Nearly every row:
+//     r_up, the nearest float32 above 1/s (so exact ties of x / s round away
+//     from zero), and one fused multiply-add rounding x r_up to nearest even,
+//     RN(x r_up + 1.5 2^23), the code in its low byte (x r_up is never an
+//     exact tie when r_up has at least 9 significant bits); rows whose r is
+//     a power of two: trunc(RN(x r + copysign(0.5 - 2^-25, x))), exactly
+//     round half away of x / s.  Either equals round(x / s) except within
+//     a few ulp of a half-integer; rows
+//     with a tiny absmax are pre-scaled by 2^64 so that 1/s cannot overflow;
+//     the int8 codes leave as 16-byte stores.
 //
 // Fast path (pack_rows_kernel), used when G <= 1024 and K is a multiple of
 // 1024 (every row then splits into whole 64-chunk wave loads): one wave owns
@@ -235,20 +239,43 @@ CR_DEVICE void load_rotate_segment(const InT* __restrict__ xr, int seg, int nch,
   }
 }
 
+// How a row's codes are decided (uniform per row):
+//   kCodeNearestEven: code_bits_rne(x, r_up), one operation.  r_up is the
+//     smallest float32 above 1/s among r = RN(1/s) and r + 1 ulp (the sign
+//     of the exact residual fma(-s, r, 1) tells which side of 1/s r lies):
+//     where x / s is exactly a half-integer, x r_up lies strictly above it
+//     and rounds away from zero, as the oracle's decision does; r_up has at
+//     least 9 significant bits, so x r_up itself is never an exact tie.
+//     Values within one ulp of r_up (relative) below a half-integer also
+//     round up, as values within half an ulp do in the oracle's float32
+//     quotient: a rounding-tie difference.
+//   kCodeHalfAway: code_of(x, r), for r = 0 and powers of two (x r is then
+//     exact and the decision exactly round half away of x / s, as at unit
+//     scale) and the rare r_up without 9 significant bits.
+//   kCodeTiny: tiny rows (pre-scaled and clamped).
+enum { kCodeNearestEven = 0, kCodeHalfAway = 1, kCodeTiny = 2 };
+
 // Scale of a row from the absmax mx of its unnormalised rotation (2^n X_rot):
-// s = (mx 2^-n) / 127, the value stored.  Returns s; sets r = RN(1 / s_un),
-// the reciprocal the codes use (s_un = s 2^n, so x_un / s_un == x / s
-// exactly), with r = 0 for a zero row.  Rows whose absmax is below
-// kTinyRowMax are "tiny": r is formed for s_un 2^64 instead, and their
-// values must be multiplied by 2^64 (exactly) and their codes clamped.
-CR_DEVICE float row_scale(float mx, int log4g, float& r, bool& tiny) {
+// s = (mx 2^-n) / 127, the value stored.  Returns s; sets the row's code
+// decision and r, the multiplier it uses: RN(1 / s_un) (s_un = s 2^n, so
+// x_un / s_un == x / s exactly; 0 for a zero row), or r_up for
+// kCodeNearestEven.  Rows
+// whose absmax is below kTinyRowMax are "tiny": r is formed for s_un 2^64
+// instead, and their values must be multiplied by 2^64 (exactly) and their
+// codes clamped.
+CR_DEVICE float row_scale(float mx, int log4g, float& r, int& mode) {
   mx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mx)));  // uniform: one per row
   const float m = ldexpf(mx, -log4g);
   const float s = m / 127.0f;
-  tiny = m < kTinyRowMax;
+  const bool tiny = m < kTinyRowMax;
   float s_un = ldexpf(s, log4g);
   if (tiny) s_un *= kTinyRowScale;
   r = (s_un != 0.f) ? 1.0f / s_un : 0.f;
+  const float r_up =
+      __uint_as_float(__float_as_uint(r) + (__builtin_fmaf(-s_un, r, 1.0f) > 0.f ? 1u : 0u));
+  const bool nearest = !tiny && (__float_as_uint(r) & 0x7FFFFFu) != 0u && no_exact_ties(r_up);
+  mode = __builtin_amdgcn_readfirstlane(tiny ? kCodeTiny : nearest ? kCodeNearestEven : kCodeHalfAway);
+  if (nearest) r = r_up;
   return s;
 }
 
@@ -263,7 +290,7 @@ CR_DEVICE float local_absmax(const float (&v)[CPT][16]) {
 }
 
 template <int CPT>
-CR_DEVICE void quantize_store(float (&v)[CPT][16], int seg, int nch, float r, bool tiny,
+CR_DEVICE void quantize_store(float (&v)[CPT][16], int seg, int nch, float r, int mode,
                               int8_t* __restrict__ qr, int t, int T) {
   const int tp = chunk_of_thread(t);
 #pragma unroll
@@ -271,7 +298,10 @@ CR_DEVICE void quantize_store(float (&v)[CPT][16], int seg, int nch, float r, bo
     const int j = (seg * CPT + c) * T + tp;
     if (j >= nch) continue;
     int qi[16];
-    if (!tiny) {
+    if (mode == kCodeNearestEven) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) qi[e] = code_bits_rne(v[c][e], r);
+    } else if (mode == kCodeHalfAway) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) qi[e] = code_of(v[c][e], r);
     } else {
@@ -317,16 +347,16 @@ __global__ __launch_bounds__(1024) void pack_kernel(const InT* __restrict__ x, i
     for (int w = 1; w < nwaves; ++w) mx = fmaxf(mx, wave_max[w]);
     __syncthreads();  // wave_max is rewritten for the next row
 
-    bool tiny;
+    int mode;
     float r;
-    const float s = row_scale(mx, log4g, r, tiny);
+    const float s = row_scale(mx, log4g, r, mode);
     if (t == 0) scale[row] = s;
     if (nseg == 1) {
-      quantize_store<CPT>(v, 0, nch, r, tiny, qr, t, T);
+      quantize_store<CPT>(v, 0, nch, r, mode, qr, t, T);
     } else {
       for (int seg = 0; seg < nseg; ++seg) {
         load_rotate_segment<InT, CPT>(xr, seg, nch, log4g, v, lds_buf, t, T);
-        quantize_store<CPT>(v, seg, nch, r, tiny, qr, t, T);
+        quantize_store<CPT>(v, seg, nch, r, mode, qr, t, T);
       }
     }
   }
@@ -512,15 +542,18 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const InT* __restrict__ 
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(v[c][e]));
     mx = wave_max_nonneg(mx);
-    bool tiny;
+    int mode;
     float r;
-    const float s = row_scale(mx, log4g, r, tiny);
+    const float s = row_scale(mx, log4g, r, mode);
     if (lane == 0) scale[row] = s;
     int8_t* qr = q + (int64_t)row * k;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       int qi[16];
-      if (!tiny) {
+      if (mode == kCodeNearestEven) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) qi[e] = code_bits_rne(v[c][e], r);
+      } else if (mode == kCodeHalfAway) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) qi[e] = code_of(v[c][e], r);
       } else {
@@ -543,9 +576,9 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const InT* __restrict__ 
 // exchange is LDS traffic instead of VALU work.  The codes return to the
 // natural layout by a byte transpose through the same LDS buffer and leave
 // as 16-byte stores.  For a row whose absmax m is not tiny, every |x| <= m
-// and r = RN(1 / RN(m / 127)), so |x r| <= 127 (1 + 2^-23) and
-// trunc(RN(|x r| + 0.5 - 2^-25)) <= 127: the code needs no clamp (tiny rows,
-// whose subnormal scale may be rounded by far more, take the clamped path).
+// and r = RN(1 / RN(m / 127)), so |x r| <= 127 (1 + 2^-23), which either
+// decision rounds to at most 127: the code needs no clamp (tiny rows, whose
+// subnormal scale may be rounded by far more, take the clamped path).
 // The 16 x 16 float transpose of a 16-lane group: lane li writes its 16
 // values as row li (four 16-byte writes) and reads column li back.  Rows are
 // kTRow = 20 floats apart, so the 16 row starts of a write fall on 16
@@ -640,9 +673,9 @@ __global__ __launch_bounds__(256) void pack_rows_lds_kernel(const InT* __restric
       for (int w2 = 0; w2 < WPR; ++w2) mx = fmaxf(mx, red[it & 1][(wv / WPR) * WPR + w2]);
     }
     if (!live) continue;
-    bool tiny;
+    int mode;
     float r;
-    const float s = row_scale(mx, log4g, r, tiny);
+    const float s = row_scale(mx, log4g, r, mode);
     if (lane == 0 && part == 0) scale[row] = s;
     // The codes go back to the natural layout through LDS as bytes (lane li
     // writes byte li of each of its 16 chunks; lane li then reads chunk li
@@ -653,7 +686,10 @@ __global__ __launch_bounds__(256) void pack_rows_lds_kernel(const InT* __restric
     int8_t* qr = q + (int64_t)row * k + col0 + (16 * grp + li) * 16;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      if (!tiny) {
+      if (mode == kCodeNearestEven) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tb[i * 16 + li] = (int8_t)code_bits_rne(t[c][i], r);
+      } else if (mode == kCodeHalfAway) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) tb[i * 16 + li] = (int8_t)code_of(t[c][i], r);
       } else {

@@ -42,6 +42,9 @@ def emu(tmp_path_factory):
     lib = ctypes.CDLL(out)
     lib.round_step_mismatches.restype = ctypes.c_longlong
     lib.round_step_mismatches.argtypes = [ctypes.c_float, ctypes.c_uint32, ctypes.c_uint32]
+    lib.rne_step_mismatches.restype = ctypes.c_longlong
+    lib.rne_step_mismatches.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_long,
+                                        ctypes.c_uint64]
     lib.emulate_row.restype = None
     lib.emulate_row.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_int, ctypes.c_void_p,
                                 ctypes.c_void_p]
@@ -70,6 +73,63 @@ def test_round_step_check_has_teeth(emu):
     lo, hi = _bits(0.4999), _bits(0.5001)
     assert emu.round_step_mismatches(0.5, lo, hi) > 0
     assert emu.round_step_mismatches(HALF, lo, hi) == 0
+
+
+def _rne_mismatches(lib, rs, xs_per_r=2000, seed=1):
+    rs = np.ascontiguousarray(rs, dtype=np.float32)
+    return lib.rne_step_mismatches(rs.ctypes.data, rs.size, xs_per_r, seed)
+
+
+def test_rne_step_exact_when_r_has_nine_bits(emu):
+    """r with at least 9 significant bits (low 16 encoding bits not all zero):
+    the low byte of RN(x r + 1.5 2^23) is round half away from zero of the
+    exact product for every x -- no exact ties exist -- checked on the x
+    nearest every half-integer and on random x, for random r over 2^-20..2^20
+    and for the reciprocals r = RN(1/s) of scales s = RN(m/127) of random
+    maxima m."""
+    rng = np.random.default_rng(7)
+    bits = (rng.integers(127 - 20, 127 + 20, 3000).astype(np.uint32) << 23) | \
+        rng.integers(0, 1 << 23, 3000).astype(np.uint32)
+    rs = bits.view(np.float32)
+    m = rng.lognormal(0.0, 3.0, 3000).astype(np.float32)
+    rs2 = (np.float32(1.0) / (m / np.float32(127.0))).astype(np.float32)
+    rs = np.concatenate([rs, rs2])
+    rs = rs[(rs.view(np.uint32) & 0xFFFF) != 0]
+    assert rs.size > 5900
+    assert _rne_mismatches(emu, rs) == 0
+
+
+def test_exact_ties_round_away_at_any_scale(emu):
+    """x / s exactly a half-integer at a scale that is not a power of two:
+    the row's codes are decided with r raised by two ulps (above 1 / s), so
+    every such tie rounds away from zero as the oracle's does.  Scales with
+    at most 16 significant bits make (k + 1/2) s exactly representable; each
+    row holds 127 s (its maximum, so its scale is s) and ties for k = -127 ..
+    126."""
+    rng = np.random.default_rng(11)
+    for _ in range(400):
+        e = int(rng.integers(-30, 30))
+        mant = (int(rng.integers(1 << 15, 1 << 16)) | 1) << 8  # 16 significant bits, odd part > 255
+        s32 = np.float32(np.ldexp(mant / float(1 << 23), e))
+        ks = np.arange(-127, 127)
+        xt = ((ks + 0.5) * np.float64(s32)).astype(np.float32)
+        assert np.array_equal(xt.astype(np.float64), (ks + 0.5) * np.float64(s32))  # exact ties
+        row = np.concatenate([[np.float32(127.0) * s32], xt]).astype(np.float32)
+        m = float(row.astype(np.float64).__abs__().max())
+        q, sc = emulate(emu, row[None, :], 0)
+        if sc[0] != s32:
+            continue  # m / 127 rounded to another scale: not this case
+        want = np.where(ks >= 0, ks + 1, ks)  # half away from zero
+        assert np.array_equal(q[0, 1:].astype(np.int64), want), (s32, m)
+
+
+def test_rne_step_check_has_teeth(emu):
+    """For r with fewer significant bits exact ties exist and nearest-even
+    differs from half away (which is why such rows take the other decision):
+    the check must see that."""
+    for r in (1.0, 2.0, 0.5, 1.5, 3.0, 0.75):
+        assert (int(np.float32(r).view(np.uint32)) & 0xFFFF) == 0
+        assert _rne_mismatches(emu, [r], xs_per_r=0) > 0, r
 
 
 def _exact_quotient(x32, s32):
