@@ -163,12 +163,21 @@ CR_DEVICE TileInfo tile_info(const GemmParams& p, int t) {
   const int in = t - g * per_group;
   const int tm = first + in % gm;
   const int tn = in / gm;
-  int s = 0;
-  for (int i = 1; i < p.nseg; ++i)
-    if (tn >= p.seg[i].tn0) s = i;
+  // The segment: unrolled over every slot so that the first-column loads are
+  // independent scalar loads issued together (a loop up to nseg waits for
+  // each one in turn); segment 0 starts at column 0.
+  int s = 0, tn0 = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGemmGroup; ++i) {
+    const int t0 = p.seg[i].tn0;
+    if (i < p.nseg && tn >= t0) {
+      s = i;
+      tn0 = t0;
+    }
+  }
   TileInfo ti;
   ti.m0 = tm * kBM;
-  ti.n0 = (tn - p.seg[s].tn0) * BN;
+  ti.n0 = (tn - tn0) * BN;
   ti.s = s;
   return ti;
 }
