@@ -21,7 +21,8 @@
 //   * the butterfly is unnormalised, y_d = sum(x) - 2 x_{3-d} = 2 (H4 x)_d; the
 //     factor 2^n is exact and is taken out of the scale, so every rounding is
 //     that of the normalised butterfly;
-//   * the row absmax is reduced across lanes and then across waves in LDS;
+//   * the row absmax is reduced across the wave in registers (DPP moves and
+//     permlane swaps) and then, for rows split over waves, in LDS;
 //   * the code decision is made in float32: s = m/127 (IEEE division) and
 //     r = RN(1/s) once per row, then per value a code.  Nearly every row:
 //     r_up, the nearest float32 above 1/s (so exact ties of x / s round away
@@ -30,9 +31,9 @@
 //     exact tie when r_up has at least 9 significant bits); rows whose r is
 //     a power of two: trunc(RN(x r + copysign(0.5 - 2^-25, x))), exactly
 //     round half away of x / s.  Either equals round(x / s) except within
-//     a few ulp of a half-integer; rows
-//     with a tiny absmax are pre-scaled by 2^64 so that 1/s cannot overflow;
-//     the int8 codes leave as 16-byte stores.
+//     a few ulp of a half-integer; rows with a tiny absmax are pre-scaled by
+//     2^64 so that 1/s cannot overflow; the int8 codes leave as 16-byte
+//     stores.
 //
 // Fast path (pack_rows_kernel), used when G <= 1024 and K is a multiple of
 // 1024 (every row then splits into whole 64-chunk wave loads): one wave owns
