@@ -49,7 +49,8 @@
 //     Output stores are non-temporal: Y is written once and should not push
 //     the operand slices the other CUs of the XCD still read out of L2.
 //   * s_x, s_w and b of a tile reach LDS by direct-to-LDS loads in the tile's
-//     prologue, in a ring of two buffers.
+//     prologue (the first tile's with the first operand loads), in a ring of
+//     two buffers.
 //   * Loads and stores share one in-order counter (vmcnt).  Every wait names
 //     exactly the number of instructions issued after the awaited loads (this
 //     step's stores and the Q_w loads of two steps ahead).
@@ -461,29 +462,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
   };
 
   // ------------------------------------------------------------ prologue
-  // Q_x of step 0, Q_w of steps 0 and 1; after the barrier the first Q_x
-  // pieces of step 1.  Only step 0's operands are waited for here: Q_w of
-  // step 1 (the last WPW loads) lands under step 0, whose closing wait
-  // covers it.
-#pragma unroll
-  for (int i = 0; i < C::XPW; ++i) piece_x(i);
-  end_x();
+  // The first tile's scales and bias, then both operands of steps 0 and 1
+  // (both Q_x stages are free at the start, so the kernel's first step need
+  // not request the rest of step 1 itself: one cold-load latency instead of
+  // two before the loop runs).  Only step 0's operands (and the parameters)
+  // are waited for here: step 1's land under step 0, whose closing wait
+  // covers them.
+  issue_params(0);
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+    for (int i = 0; i < C::XPW; ++i) piece_x(i);
+    end_x();
     begin_w();
 #pragma unroll
     for (int i = 0; i < C::WPW; ++i) piece_w(i);
     end_w();
   }
-  waitvm<C::WPW>();
+  waitvm<C::XPW + C::WPW>();
   wait_lgkm0();
   barrier();
 #pragma unroll
   for (int f = 0; f < FM; ++f) read_x(smem, f, 0);
 #pragma unroll
   for (int f = 0; f < FN; ++f) read_w(smem + C::WOFF, 0, f, 0);
-#pragma unroll
-  for (int i = 0; i < C::XT; ++i) piece_x(i);
 
   int cur_x = 0, cur_w = 0;  // stages of the step being computed
 
@@ -491,8 +493,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
   // computes from Q_x stage g%2 and Q_w stage g%3; during it the rest of Q_x
   // of step g+1 and all of Q_w of step g+2 are requested.  SG >= 0: the step
   // also stores groups 2*SG and 2*SG+1 of the pending tile (fast path).
-  auto step = [&](auto first_t, auto ss_t) __attribute__((always_inline)) {
+  // PRO: the kernel's first step, whose step g+1 the prologue loaded whole.
+  auto step = [&](auto first_t, auto ss_t, auto pro_t) __attribute__((always_inline)) {
     constexpr bool FIRST = decltype(first_t)::value;
+    constexpr bool PRO = decltype(pro_t)::value;
     constexpr int SS = decltype(ss_t)::value;   // storing step index, or -1
     constexpr bool STORE = SS >= 0;
     constexpr int GPS = C::GPS;
@@ -556,13 +560,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
       __builtin_amdgcn_sched_barrier(0);
       reads_after(idx, cx, cw, 1);
       read_parked(0, idx);
-      {
+      if constexpr (!PRO) {
         const int pc = spread_piece(idx, 0, C::NMF, C::XPW - C::XT);
         if (pc >= 0) piece_x(C::XT + pc);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    end_x();
+    if constexpr (!PRO) end_x();
     begin_w();
     __builtin_amdgcn_sched_barrier(0);
 
@@ -731,7 +735,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
       const int t1 = it + 1 < ntiles ? it + 1 : ntiles - 1;
       xs.next = x_rsrc(t1);
       ws.next = w_rsrc(t1);
-      issue_params(it);
+      if (it > 0) issue_params(it);  // (the first tile's: in the kernel prologue)
       wait_lgkm0();  // no scalar load stays in flight into the K loop
     }
     if (pd_fast) {
@@ -739,9 +743,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
       // tile's first NSS steps (unrolled: constant register indices).
       for_each_index(std::make_integer_sequence<int, NSS>{}, [&](auto ss) {
         constexpr int S = decltype(ss)::value;
-        if (S < nk) step(std::integral_constant<bool, S == 0>{}, ss);
+        if (S < nk) step(std::integral_constant<bool, S == 0>{}, ss, std::false_type{});
       });
-      for (int ks = NSS; ks < nk; ++ks) step(std::false_type{}, std::integral_constant<int, -1>{});
+      for (int ks = NSS; ks < nk; ++ks)
+        step(std::false_type{}, std::integral_constant<int, -1>{}, std::false_type{});
       if (nk < NSS) {  // short K: the groups left over
         load_sw_b();
         for_each_index(std::make_integer_sequence<int, NG>{}, [&](auto qc) {
@@ -759,8 +764,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const GemmParams p
           store_group(Q, read_group_sx(Q));
         });
       }
-      step(std::true_type{}, std::integral_constant<int, -1>{});
-      for (int ks = 1; ks < nk; ++ks) step(std::false_type{}, std::integral_constant<int, -1>{});
+      if (it == 0)
+        step(std::true_type{}, std::integral_constant<int, -1>{}, std::true_type{});
+      else
+        step(std::true_type{}, std::integral_constant<int, -1>{}, std::false_type{});
+      for (int ks = 1; ks < nk; ++ks)
+        step(std::false_type{}, std::integral_constant<int, -1>{}, std::false_type{});
     }
 
     // The tile is complete and the previous one fully stored: move the
