@@ -12,7 +12,7 @@ int device_cu_count();
 // Launch shape of the activation pack for a row length k (k % 16 == 0).
 struct PackPlan {
   int threads;            // workgroup size, 64..1024
-  int chunks_per_thread;  // 16-feature chunks per thread per segment (1, 2 or 4)
+  int chunks_per_thread;  // 16-feature chunks per thread per segment (1 or 2)
   int segments;           // > 1 only for very long rows: X is then read twice
 };
 PackPlan plan_pack(int64_t k);

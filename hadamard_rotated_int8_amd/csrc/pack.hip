@@ -189,11 +189,11 @@ CR_DEVICE void rotate_across_waves(float* v, int log4g, float4* buf, int t) {
     for (int i = 0; i < 4; ++i)
       buf[t * 4 + i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
     __syncthreads();
-    const int dd = (t >> sh) & 3;
+    const int dd = (t >> sh) & 3;  // uniform per wave (sh >= 6)
     const int base = t & ~(3 << sh);
-    float sum[16], rev[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) sum[e] = v[e];
+    // The sum S accumulates in v (own value first, then the other digits in
+    // order); x_{3-dd} is read back from LDS for the last step, 4 values at a
+    // time, so the stage needs no second 16-value register set.
 #pragma unroll
     for (int d2 = 0; d2 < 4; ++d2) {
       if (d2 == dd) continue;
@@ -201,20 +201,21 @@ CR_DEVICE void rotate_across_waves(float* v, int log4g, float4* buf, int t) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float4 f = buf[tt * 4 + i];
-        sum[4 * i + 0] += f.x;
-        sum[4 * i + 1] += f.y;
-        sum[4 * i + 2] += f.z;
-        sum[4 * i + 3] += f.w;
-        if (d2 == 3 - dd) {
-          rev[4 * i + 0] = f.x;
-          rev[4 * i + 1] = f.y;
-          rev[4 * i + 2] = f.z;
-          rev[4 * i + 3] = f.w;
-        }
+        v[4 * i + 0] += f.x;
+        v[4 * i + 1] += f.y;
+        v[4 * i + 2] += f.z;
+        v[4 * i + 3] += f.w;
       }
     }
+    const int tr = base | ((3 - dd) << sh);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) v[e] = __builtin_fmaf(-2.f, rev[e], sum[e]);
+    for (int i = 0; i < 4; ++i) {
+      const float4 f = buf[tr * 4 + i];
+      v[4 * i + 0] = __builtin_fmaf(-2.f, f.x, v[4 * i + 0]);
+      v[4 * i + 1] = __builtin_fmaf(-2.f, f.y, v[4 * i + 1]);
+      v[4 * i + 2] = __builtin_fmaf(-2.f, f.z, v[4 * i + 2]);
+      v[4 * i + 3] = __builtin_fmaf(-2.f, f.w, v[4 * i + 3]);
+    }
   }
 }
 
@@ -224,13 +225,13 @@ CR_DEVICE void load_rotate_segment(const InT* __restrict__ xr, int seg, int nch,
   const int tp = chunk_of_thread(t);
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
+    // Lanes past the row's last chunk load its first one (any valid address)
+    // and zero the values: no divergent branch around the load.
     const int j = (seg * CPT + c) * T + tp;
-    if (j < nch) {
-      load16(xr + (int64_t)j * 16, v[c]);
-    } else {
+    const bool ok = j < nch;
+    load16(xr + (int64_t)(ok ? j : 0) * 16, v[c]);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) v[c][e] = 0.f;
-    }
+    for (int e = 0; e < 16; ++e) v[c][e] = ok ? v[c][e] : 0.f;
   }
 #pragma unroll
   for (int c = 0; c < CPT; ++c) rotate_in_wave(v[c], log4g);
@@ -788,18 +789,15 @@ PackPlan plan_pack(int64_t k) {
   if (waves > 16) waves = 16;
   p.threads = int(waves * 64);
   const int64_t per_thread = (nch + p.threads - 1) / p.threads;
+  // At most two chunks per thread: a 1024-thread workgroup leaves each wave
+  // 128 registers, which four chunks would exceed (the compiler would spill
+  // to scratch memory).  Longer rows are taken in segments and read twice.
   if (per_thread <= 1) {
     p.chunks_per_thread = 1;
     p.segments = 1;
-  } else if (per_thread <= 2) {
-    p.chunks_per_thread = 2;
-    p.segments = 1;
-  } else if (per_thread <= 4) {
-    p.chunks_per_thread = 4;
-    p.segments = 1;
   } else {
-    p.chunks_per_thread = 4;
-    p.segments = int((per_thread + 3) / 4);
+    p.chunks_per_thread = 2;
+    p.segments = int((per_thread + 1) / 2);
   }
   return p;
 }
@@ -817,8 +815,6 @@ hipError_t launch_pack(const void* x, bool bf16, int64_t ldx, int64_t m, int64_t
     case 3: return launch_pack_t<uint16_t, 1>(x, ldx, mi, ki, log4g, p.threads, p.segments, q, scale, stream);
     case 4: return launch_pack_t<float, 2>(x, ldx, mi, ki, log4g, p.threads, p.segments, q, scale, stream);
     case 5: return launch_pack_t<uint16_t, 2>(x, ldx, mi, ki, log4g, p.threads, p.segments, q, scale, stream);
-    case 8: return launch_pack_t<float, 4>(x, ldx, mi, ki, log4g, p.threads, p.segments, q, scale, stream);
-    case 9: return launch_pack_t<uint16_t, 4>(x, ldx, mi, ki, log4g, p.threads, p.segments, q, scale, stream);
     default: return hipErrorInvalidValue;
   }
 }
